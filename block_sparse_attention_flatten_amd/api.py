@@ -1,0 +1,263 @@
+"""Python binding of libnabla: the C ABI's calls under the same names, taking
+torch tensors.  Argument marshalling only -- every step runs in the HIP
+kernels behind include/nabla.h; PyTorch provides device memory and the stream.
+
+Tensor layouts are those of the C header:
+  THW      [B, heads, T, H, W, d]      (natural latent order, valid tokens)
+  BLOCKED  [B, heads, nb, 64, d]       (fractal-flattened, padded)
+  qbar/kbar float32 [B, heads, nb, d]; mask words uint32 stored in int32
+  tensors [B, heads, nb, ceil(nb/32)]; row counts int32 [B, heads, nb];
+  row_ptr int32 [B*heads, nb+1]; col_idx int32 [B*heads, nb*nb].
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import DTYPE_BF16, DTYPE_F32, LAYOUT_BLOCKED, LAYOUT_THW, nabla_geom
+
+__all__ = [
+    "NablaError", "Geometry", "nabla_num_blocks", "nabla_flatten", "nabla_unflatten",
+    "nabla_pool", "nabla_mask", "nabla_compact", "nabla_attn_fwd",
+    "nabla_forward_workspace_size", "nabla_forward", "nabla_status_string", "forward",
+    "LAYOUT_THW", "LAYOUT_BLOCKED",
+]
+
+
+class NablaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = _lib.load()
+        text = lib.nabla_status_string(status).decode()
+        extra = ""
+        if status == -10:
+            extra = f" (hipError {lib.nabla_last_hip_error()})"
+        super().__init__(f"{where}: {_lib.STATUS.get(status, status)}: {text}{extra}")
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != _lib.NABLA_OK:
+        raise NablaError(status, where)
+
+
+_DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
+
+
+@dataclass(frozen=True)
+class Geometry:
+    """Shape of one call (mirrors nabla_geom)."""
+
+    batch: int
+    heads: int
+    T: int
+    H: int
+    W: int
+    head_dim: int
+    dtype: torch.dtype
+    layout: int = LAYOUT_THW
+    P: int = 8
+
+    @property
+    def gh(self) -> int:
+        return -(-self.H // self.P)
+
+    @property
+    def gw(self) -> int:
+        return -(-self.W // self.P)
+
+    @property
+    def nb(self) -> int:
+        return self.T * self.gh * self.gw
+
+    @property
+    def nw(self) -> int:
+        return -(-self.nb // 32)
+
+    def c(self) -> nabla_geom:
+        return nabla_geom(self.batch, self.heads, self.T, self.H, self.W, self.P, self.head_dim,
+                          _DT.get(self.dtype, -1), self.layout)
+
+    def tensor_shape(self, layout: Optional[int] = None) -> Tuple[int, ...]:
+        lay = self.layout if layout is None else layout
+        if lay == LAYOUT_THW:
+            return (self.batch, self.heads, self.T, self.H, self.W, self.head_dim)
+        return (self.batch, self.heads, self.nb, 64, self.head_dim)
+
+    def with_layout(self, layout: int) -> "Geometry":
+        return Geometry(self.batch, self.heads, self.T, self.H, self.W, self.head_dim,
+                        self.dtype, layout, self.P)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, shape=None, dtype=None) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _sta(sta: Optional[Sequence[int]]):
+    if sta is None:
+        return None
+    arr = (ctypes.c_int32 * 3)(*[int(x) for x in sta])
+    return arr
+
+
+def nabla_status_string(status: int) -> str:
+    return _lib.load().nabla_status_string(status).decode()
+
+
+def nabla_num_blocks(g: Geometry) -> int:
+    out = ctypes.c_int64(0)
+    _check(_lib.load().nabla_num_blocks(ctypes.byref(g.c()), ctypes.byref(out)),
+           "nabla_num_blocks")
+    return out.value
+
+
+def nabla_flatten(g: Geometry, x: torch.Tensor, x_blocked: torch.Tensor, stream=None) -> None:
+    lib = _lib.load()
+    _check(lib.nabla_flatten(ctypes.byref(g.c()),
+                             _ptr(x, "x", g.tensor_shape(LAYOUT_THW), g.dtype),
+                             _ptr(x_blocked, "x_blocked", g.tensor_shape(LAYOUT_BLOCKED), g.dtype),
+                             _stream(stream)), "nabla_flatten")
+
+
+def nabla_unflatten(g: Geometry, x_blocked: torch.Tensor, x: torch.Tensor, stream=None) -> None:
+    lib = _lib.load()
+    _check(lib.nabla_unflatten(ctypes.byref(g.c()),
+                               _ptr(x_blocked, "x_blocked", g.tensor_shape(LAYOUT_BLOCKED),
+                                    g.dtype),
+                               _ptr(x, "x", g.tensor_shape(LAYOUT_THW), g.dtype),
+                               _stream(stream)), "nabla_unflatten")
+
+
+def nabla_pool(g: Geometry, q, k, qbar, kbar, stream=None) -> None:
+    shp = g.tensor_shape()
+    pshape = (g.batch, g.heads, g.nb, g.head_dim)
+    _check(_lib.load().nabla_pool(
+        ctypes.byref(g.c()), _ptr(q, "q", shp, g.dtype), _ptr(k, "k", shp, g.dtype),
+        _ptr(qbar, "qbar", pshape, torch.float32), _ptr(kbar, "kbar", pshape, torch.float32),
+        _stream(stream)), "nabla_pool")
+
+
+def nabla_mask(g: Geometry, qbar, kbar, thr: float, sta, mask_bits, row_count,
+               adaptive_bits=None, stream=None) -> None:
+    pshape = (g.batch, g.heads, g.nb, g.head_dim)
+    mshape = (g.batch, g.heads, g.nb, g.nw)
+    _check(_lib.load().nabla_mask(
+        ctypes.byref(g.c()), _ptr(qbar, "qbar", pshape, torch.float32),
+        _ptr(kbar, "kbar", pshape, torch.float32), float(thr), _sta(sta),
+        _ptr(mask_bits, "mask_bits", mshape, torch.int32),
+        _ptr(row_count, "row_count", (g.batch, g.heads, g.nb), torch.int32),
+        _ptr(adaptive_bits, "adaptive_bits", mshape, torch.int32), _stream(stream)),
+        "nabla_mask")
+
+
+def nabla_compact(g: Geometry, mask_bits, row_count, row_ptr, col_idx, stream=None) -> None:
+    bh = g.batch * g.heads
+    _check(_lib.load().nabla_compact(
+        ctypes.byref(g.c()),
+        _ptr(mask_bits, "mask_bits", (g.batch, g.heads, g.nb, g.nw), torch.int32),
+        _ptr(row_count, "row_count", (g.batch, g.heads, g.nb), torch.int32),
+        _ptr(row_ptr, "row_ptr", (bh, g.nb + 1), torch.int32),
+        _ptr(col_idx, "col_idx", (bh, g.nb * g.nb), torch.int32), _stream(stream)),
+        "nabla_compact")
+
+
+def nabla_attn_fwd(g: Geometry, q, k, v, row_ptr, col_idx, scale: float, o, stream=None) -> None:
+    shp = g.tensor_shape()
+    bh = g.batch * g.heads
+    _check(_lib.load().nabla_attn_fwd(
+        ctypes.byref(g.c()), _ptr(q, "q", shp, g.dtype), _ptr(k, "k", shp, g.dtype),
+        _ptr(v, "v", shp, g.dtype), _ptr(row_ptr, "row_ptr", (bh, g.nb + 1), torch.int32),
+        _ptr(col_idx, "col_idx", (bh, g.nb * g.nb), torch.int32), float(scale),
+        _ptr(o, "o", shp, g.dtype), _stream(stream)), "nabla_attn_fwd")
+
+
+def nabla_forward_workspace_size(g: Geometry) -> Tuple[int, Tuple[int, ...]]:
+    size = ctypes.c_size_t(0)
+    offs = (ctypes.c_size_t * 6)()
+    _check(_lib.load().nabla_forward_workspace_size(ctypes.byref(g.c()), ctypes.byref(size),
+                                                    offs), "nabla_forward_workspace_size")
+    return size.value, tuple(offs)
+
+
+def nabla_forward(g: Geometry, q, k, v, thr: float, sta, scale: float, o, workspace,
+                  stream=None) -> None:
+    shp = g.tensor_shape()
+    _check(_lib.load().nabla_forward(
+        ctypes.byref(g.c()), _ptr(q, "q", shp, g.dtype), _ptr(k, "k", shp, g.dtype),
+        _ptr(v, "v", shp, g.dtype), float(thr), _sta(sta), float(scale),
+        _ptr(o, "o", shp, g.dtype), _ptr(workspace, "workspace", None, torch.uint8),
+        workspace.numel(), _stream(stream)), "nabla_forward")
+
+
+# ---------------------------------------------------------------------------
+# convenience: allocate outputs/workspace with torch and run the whole call
+# ---------------------------------------------------------------------------
+@dataclass
+class ForwardResult:
+    o: torch.Tensor
+    qbar: torch.Tensor
+    kbar: torch.Tensor
+    mask_bits: torch.Tensor
+    row_count: torch.Tensor
+    row_ptr: torch.Tensor
+    col_idx: torch.Tensor
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, thr: float,
+            sta: Optional[Sequence[int]] = (3, 3, 3), scale: Optional[float] = None,
+            layout: int = LAYOUT_THW, T: Optional[int] = None, H: Optional[int] = None,
+            W: Optional[int] = None, stream=None) -> ForwardResult:
+    """One NABLA attention call.  THW tensors carry T, H, W in their shape;
+    BLOCKED tensors need T, H, W passed explicitly."""
+    if layout == LAYOUT_THW:
+        B, h, T, H, W, d = q.shape
+    else:
+        B, h, _, _, d = q.shape
+        if T is None or H is None or W is None:
+            raise ValueError("T, H, W are required for the blocked layout")
+    g = Geometry(B, h, T, H, W, d, q.dtype, layout)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    size, offs = nabla_forward_workspace_size(g)
+    ws = torch.empty(size, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    nabla_forward(g, q, k, v, thr, sta, scale, o, ws, stream)
+
+    def part(i, dtype, shape):
+        n = math.prod(shape)
+        esz = torch.tensor([], dtype=dtype).element_size()
+        return ws[offs[i]:offs[i] + n * esz].view(dtype).view(shape)
+
+    bh = B * h
+    return ForwardResult(
+        o=o,
+        qbar=part(0, torch.float32, (B, h, g.nb, d)),
+        kbar=part(1, torch.float32, (B, h, g.nb, d)),
+        mask_bits=part(2, torch.int32, (B, h, g.nb, g.nw)),
+        row_count=part(3, torch.int32, (B, h, g.nb)),
+        row_ptr=part(4, torch.int32, (bh, g.nb + 1)),
+        col_idx=part(5, torch.int32, (bh, g.nb * g.nb)),
+    )

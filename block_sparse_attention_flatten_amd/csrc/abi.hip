@@ -1,0 +1,259 @@
+// C ABI of libnabla (declared in include/nabla.h): argument validation,
+// geometry derivation and kernel launches.  Every check runs before anything
+// is enqueued; no entry point allocates memory, synchronizes or throws.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/nabla.h"
+#include "nabla_common.hpp"
+
+using nabla::Geo;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return NABLA_OK;
+  g_last_hip_error = (int)e;
+  return NABLA_E_HIP;
+}
+
+// Validate the geometry and derive the kernels' view of it.  `layout_used`
+// is false for entry points whose tensor layout is fixed by the call.
+int make_geo(const nabla_geom* p, bool layout_used, Geo* g, bool* empty) {
+  if (p == nullptr) return NABLA_E_NULL;
+  if (p->batch < 0 || p->heads < 0) return NABLA_E_SHAPE;
+  if (p->T < 1 || p->H < 1 || p->W < 1) return NABLA_E_SHAPE;
+  if (p->P != nabla::kP) return NABLA_E_PATCH;
+  if (p->head_dim != 64 && p->head_dim != 128) return NABLA_E_HEAD_DIM;
+  if (p->dtype != NABLA_DTYPE_F32 && p->dtype != NABLA_DTYPE_BF16) return NABLA_E_DTYPE;
+  if (layout_used && p->layout != NABLA_LAYOUT_THW && p->layout != NABLA_LAYOUT_BLOCKED)
+    return NABLA_E_LAYOUT;
+  const int64_t gh = (p->H + 7) / 8, gw = (p->W + 7) / 8;
+  if (p->H > (1 << 20) || p->W > (1 << 20) || p->T > (1 << 20)) return NABLA_E_SHAPE;
+  const int64_t nb = (int64_t)p->T * gh * gw;
+  if (nb > NABLA_MAX_BLOCKS) return NABLA_E_TOO_LARGE;
+  const int64_t bh = p->batch * p->heads;
+  if (p->batch != 0 && bh / p->batch != p->heads) return NABLA_E_SHAPE;
+  if (bh > 65535) return NABLA_E_SHAPE;             // one grid row per head in the mask kernels
+  const int64_t thw = (int64_t)p->T * p->H * p->W * p->head_dim;
+  const int64_t blk = nb * nabla::kN * p->head_dim;
+  if (thw >= (int64_t)1 << 31 || blk >= (int64_t)1 << 31) return NABLA_E_SHAPE;
+  g->bh = bh;
+  g->T = p->T;
+  g->H = p->H;
+  g->W = p->W;
+  g->gh = (int)gh;
+  g->gw = (int)gw;
+  g->nb = (int)nb;
+  g->d = p->head_dim;
+  g->layout = p->layout == NABLA_LAYOUT_BLOCKED ? 1 : 0;
+  g->head_elems = (int)(g->layout == 1 ? blk : thw);
+  *empty = bh == 0;
+  return NABLA_OK;
+}
+
+int check_sta(const int32_t* sta, int out[3]) {
+  out[0] = out[1] = out[2] = 0;
+  if (sta == nullptr) return NABLA_OK;
+  const bool all_zero = sta[0] == 0 && sta[1] == 0 && sta[2] == 0;
+  if (all_zero) return NABLA_OK;
+  for (int i = 0; i < 3; ++i) {
+    if (sta[i] <= 0 || (sta[i] & 1) == 0) return NABLA_E_STA;
+    out[i] = sta[i];
+  }
+  return NABLA_OK;
+}
+
+bool thr_ok(float thr) { return isfinite(thr) && thr > 0.0f && thr <= 1.0f; }
+bool scale_ok(float s) { return isfinite(s) && s > 0.0f; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+void workspace_parts(const Geo& g, size_t off[6], size_t* total) {
+  const size_t bh = (size_t)g.bh, nb = (size_t)g.nb, nw = (nb + 31) / 32;
+  const size_t sizes[6] = {
+      bh * nb * g.d * sizeof(float),        // qbar
+      bh * nb * g.d * sizeof(float),        // kbar
+      bh * nb * nw * sizeof(uint32_t),      // mask bits
+      bh * nb * sizeof(int32_t),            // row counts
+      bh * (nb + 1) * sizeof(int32_t),      // row_ptr
+      bh * nb * nb * sizeof(int32_t),       // col_idx
+  };
+  size_t at = 0;
+  for (int i = 0; i < 6; ++i) {
+    off[i] = at;
+    at = align256(at + sizes[i]);
+  }
+  *total = at;
+}
+
+hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+}  // namespace
+
+extern "C" {
+
+int nabla_abi_version(void) { return NABLA_ABI_VERSION; }
+
+int nabla_last_hip_error(void) { return g_last_hip_error; }
+
+const char* nabla_status_string(int status) {
+  switch (status) {
+    case NABLA_OK: return "ok";
+    case NABLA_E_NULL: return "a required pointer is NULL";
+    case NABLA_E_SHAPE: return "invalid shape (batch/heads < 0, T/H/W < 1, or sizes beyond the limits)";
+    case NABLA_E_DTYPE: return "dtype must be NABLA_DTYPE_F32 or NABLA_DTYPE_BF16";
+    case NABLA_E_HEAD_DIM: return "head_dim must be 64 or 128";
+    case NABLA_E_PATCH: return "patch side P must be 8";
+    case NABLA_E_THR: return "thr must be finite and in (0, 1]";
+    case NABLA_E_STA: return "STA window must be {0,0,0} or three positive odd sizes";
+    case NABLA_E_WORKSPACE: return "workspace smaller than nabla_forward_workspace_size";
+    case NABLA_E_LAYOUT: return "layout must be NABLA_LAYOUT_THW or NABLA_LAYOUT_BLOCKED";
+    case NABLA_E_HIP: return "HIP launch failed (see nabla_last_hip_error)";
+    case NABLA_E_SCALE: return "softmax scale must be finite and > 0";
+    case NABLA_E_TOO_LARGE: return "more blocks per head than NABLA_MAX_BLOCKS";
+    default: return "unknown status";
+  }
+}
+
+int nabla_num_blocks(const nabla_geom* geom, int64_t* nb) {
+  Geo g;
+  bool empty;
+  const int st = make_geo(geom, false, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (nb == nullptr) return NABLA_E_NULL;
+  *nb = g.nb;
+  return NABLA_OK;
+}
+
+int nabla_flatten(const nabla_geom* geom, const void* x, void* x_blocked, void* stream) {
+  Geo g;
+  bool empty;
+  const int st = make_geo(geom, false, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (empty) return NABLA_OK;
+  if (x == nullptr || x_blocked == nullptr) return NABLA_E_NULL;
+  const int eb = geom->dtype == NABLA_DTYPE_BF16 ? 2 : 4;
+  return hip_status(nabla::launch_flatten(g, eb, x, x_blocked, false, as_stream(stream)));
+}
+
+int nabla_unflatten(const nabla_geom* geom, const void* x_blocked, void* x, void* stream) {
+  Geo g;
+  bool empty;
+  const int st = make_geo(geom, false, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (empty) return NABLA_OK;
+  if (x == nullptr || x_blocked == nullptr) return NABLA_E_NULL;
+  const int eb = geom->dtype == NABLA_DTYPE_BF16 ? 2 : 4;
+  return hip_status(nabla::launch_flatten(g, eb, x_blocked, x, true, as_stream(stream)));
+}
+
+int nabla_pool(const nabla_geom* geom, const void* q, const void* k, float* qbar, float* kbar,
+               void* stream) {
+  Geo g;
+  bool empty;
+  const int st = make_geo(geom, true, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (empty) return NABLA_OK;
+  if (q == nullptr || k == nullptr || qbar == nullptr || kbar == nullptr) return NABLA_E_NULL;
+  return hip_status(nabla::launch_pool(g, geom->dtype == NABLA_DTYPE_BF16, q, k, qbar, kbar,
+                                       as_stream(stream)));
+}
+
+int nabla_mask(const nabla_geom* geom, const float* qbar, const float* kbar, float thr,
+               const int32_t* sta, uint32_t* mask_bits, int32_t* row_count,
+               uint32_t* adaptive_bits, void* stream) {
+  Geo g;
+  bool empty;
+  int st = make_geo(geom, false, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (!thr_ok(thr)) return NABLA_E_THR;
+  int win[3];
+  st = check_sta(sta, win);
+  if (st != NABLA_OK) return st;
+  if (empty) return NABLA_OK;
+  if (qbar == nullptr || kbar == nullptr || mask_bits == nullptr || row_count == nullptr)
+    return NABLA_E_NULL;
+  return hip_status(nabla::launch_mask(g, qbar, kbar, thr, win, mask_bits, row_count,
+                                       adaptive_bits, as_stream(stream)));
+}
+
+int nabla_compact(const nabla_geom* geom, const uint32_t* mask_bits, const int32_t* row_count,
+                  int32_t* row_ptr, int32_t* col_idx, void* stream) {
+  Geo g;
+  bool empty;
+  const int st = make_geo(geom, false, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (empty) return NABLA_OK;
+  if (mask_bits == nullptr || row_count == nullptr || row_ptr == nullptr || col_idx == nullptr)
+    return NABLA_E_NULL;
+  return hip_status(
+      nabla::launch_compact(g, mask_bits, row_count, row_ptr, col_idx, as_stream(stream)));
+}
+
+int nabla_attn_fwd(const nabla_geom* geom, const void* q, const void* k, const void* v,
+                   const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
+                   void* stream) {
+  Geo g;
+  bool empty;
+  const int st = make_geo(geom, true, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (!scale_ok(scale)) return NABLA_E_SCALE;
+  if (empty) return NABLA_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || row_ptr == nullptr || col_idx == nullptr ||
+      o == nullptr)
+    return NABLA_E_NULL;
+  return hip_status(nabla::launch_attn_fwd(g, geom->dtype == NABLA_DTYPE_BF16, q, k, v, row_ptr,
+                                           col_idx, scale, o, as_stream(stream)));
+}
+
+int nabla_forward_workspace_size(const nabla_geom* geom, size_t* bytes, size_t* offsets) {
+  Geo g;
+  bool empty;
+  const int st = make_geo(geom, true, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (bytes == nullptr) return NABLA_E_NULL;
+  size_t off[6], total;
+  workspace_parts(g, off, &total);
+  *bytes = total;
+  if (offsets != nullptr) memcpy(offsets, off, sizeof(off));
+  return NABLA_OK;
+}
+
+int nabla_forward(const nabla_geom* geom, const void* q, const void* k, const void* v, float thr,
+                  const int32_t* sta, float scale, void* o, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  Geo g;
+  bool empty;
+  int st = make_geo(geom, true, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (!thr_ok(thr)) return NABLA_E_THR;
+  if (!scale_ok(scale)) return NABLA_E_SCALE;
+  int win[3];
+  st = check_sta(sta, win);
+  if (st != NABLA_OK) return st;
+  if (empty) return NABLA_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || workspace == nullptr)
+    return NABLA_E_NULL;
+  size_t off[6], total;
+  workspace_parts(g, off, &total);
+  if (workspace_bytes < total) return NABLA_E_WORKSPACE;
+  char* ws = (char*)workspace;
+  float* qbar = (float*)(ws + off[0]);
+  float* kbar = (float*)(ws + off[1]);
+  uint32_t* bits = (uint32_t*)(ws + off[2]);
+  int32_t* cnt = (int32_t*)(ws + off[3]);
+  int32_t* rp = (int32_t*)(ws + off[4]);
+  int32_t* ci = (int32_t*)(ws + off[5]);
+  const hipStream_t s = as_stream(stream);
+  const bool bf16 = geom->dtype == NABLA_DTYPE_BF16;
+  hipError_t e = nabla::launch_pool(g, bf16, q, k, qbar, kbar, s);
+  if (e == hipSuccess) e = nabla::launch_mask(g, qbar, kbar, thr, win, bits, cnt, nullptr, s);
+  if (e == hipSuccess) e = nabla::launch_compact(g, bits, cnt, rp, ci, s);
+  if (e == hipSuccess) e = nabla::launch_attn_fwd(g, bf16, q, k, v, rp, ci, scale, o, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,338 @@
+// Block-sparse attention forward over the kept N x N token blocks
+// ("NABLA: Neighborhood Adaptive Block-Level Attention", gist.science,
+// Methodology: expansion of the block mask back to token resolution;
+// lsdiaocha.cn article, sec. 2 step 3: each kept reduced entry stands for a
+// whole N x N block computed exactly).
+//
+// bf16 path, gfx950 matrix cores.  One workgroup of two wavefronts computes one
+// query block (64 tokens) of one head; wavefront w owns queries 32w..32w+31.
+// For every kept key block listed in the CSR row:
+//   * the K and V tiles (64 x d bf16 each) are staged in LDS; the next tile is
+//     prefetched into registers while the current one is computed;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so that the 32 scores a lane
+//     holds all belong to ONE query (its column) -- the online softmax needs
+//     one cross-lane exchange (lane l <-> l^32) per block for the row max and
+//     none for the row sum (each lane keeps a partial sum);
+//   * P^T is converted to bf16 in registers and used directly as the B
+//     operand of O^T += V^T P^T; the contraction over the 64 keys follows the
+//     order in which the lane holds P^T, and the matching V^T elements are
+//     gathered from the row-major V tile in LDS;
+//   * the running max is only moved when a block's max exceeds it by more
+//     than 2^8 in the exp2 domain (exact: O and the row sum always share the
+//     same reference), which skips most rescales of the 64 O registers.
+// Pad keys (latent edge blocks) get -inf scores; pad queries are not written
+// (blocked layout: written as zeros).  Workgroups are remapped so that each
+// XCD walks a contiguous range of (head, query block) tiles, which keeps
+// neighbouring query blocks' K/V in that XCD's L2.
+//
+// fp32 path: a plain kernel (one thread per query, fp32 FMA, K/V tiles in
+// LDS) used for float32 inputs.
+#include "nabla_common.hpp"
+
+namespace nabla {
+
+namespace {
+
+// Workgroup id -> tile id such that XCD x (= bid % 8) gets a contiguous range.
+__device__ inline int64_t xcd_tile(int64_t bid, int64_t n) {
+  const int64_t q = n >> 3, r = n & 7;
+  const int64_t x = bid & 7, i = bid >> 3;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
+template <int D>
+struct AttnShape {
+  static constexpr int kStride = D + 8;           // LDS row stride (elements): 16 B pad
+  static constexpr int kChunks = D / 8;           // 16-byte chunks per token row
+  static constexpr int kRowsPerPass = 128 / kChunks;
+  static constexpr int kPasses = kN / kRowsPerPass;
+  static constexpr int kSteps = D / 16;           // k-steps of S^T = K Q^T
+  static constexpr int kDTiles = D / 32;          // 32-row tiles of O^T
+};
+
+template <int D>
+__global__ void __launch_bounds__(128, 2)
+attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                     const __bf16* __restrict__ V, const int32_t* __restrict__ row_ptr,
+                     const int32_t* __restrict__ col_idx, float scale_log2,
+                     __bf16* __restrict__ O) {
+  using A = AttnShape<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[kN * A::kStride];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[kN * A::kStride];
+
+  const int nb = g.nb;
+  const int64_t tile = xcd_tile(blockIdx.x, (int64_t)gridDim.x);
+  const int64_t head = tile / nb;
+  const int qb = (int)(tile - head * nb);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hl = lane >> 5;          // lane half
+  const int jl = lane & 31;          // query column / operand row of this lane
+  const int64_t hoff = head * (int64_t)g.head_elems;
+  const int row_step = block_row_step(g);
+
+  // ---- this lane's query row as the B operand of S^T = K Q^T ----
+  const int qs = 32 * wave + jl;     // slot in the query block
+  const BlockCoord qc = block_coord(g, qb);
+  const bool qvalid = (qs >> 3) < block_rows_valid(g, qc) && (qs & 7) < block_cols_valid(g, qc);
+  const int64_t qoff = hoff + block_base(g, qb, qc) + (qs >> 3) * row_step + (qs & 7) * D;
+  bf16x8 qop[A::kSteps];
+#pragma unroll
+  for (int s = 0; s < A::kSteps; ++s) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (qvalid) raw = *(const u32x4*)(Q + qoff + 16 * s + 8 * hl);
+    qop[s] = __builtin_bit_cast(bf16x8, raw);
+  }
+
+  f32x16 oacc[A::kDTiles];
+#pragma unroll
+  for (int t = 0; t < A::kDTiles; ++t) oacc[t] = f32x16{};
+  // running max (exp2 domain) of this lane's query; a finite start keeps a
+  // block whose keys are all masked (scores -inf) at p = exp2(-inf) = 0
+  float m_run = -1e30f;
+  float l_run = 0.f;                 // partial row sum over the keys this lane holds
+
+  const int32_t* rp = row_ptr + head * (nb + 1);
+  const int begin = rp[qb];
+  int end = rp[qb + 1];
+  if (begin < 0 || end < begin || end > nb * nb) end = begin;   // malformed row: no keys
+  const int32_t* cols = col_idx + head * (int64_t)nb * nb;
+
+  // loader mapping: thread -> (chunk, first row); rows advance by kRowsPerPass
+  const int ld_chunk = tid % A::kChunks;
+  const int ld_row = tid / A::kChunks;
+  u32x4 kreg[A::kPasses], vreg[A::kPasses];
+
+  auto fetch = [&](int beta) {
+    const BlockCoord bc = block_coord(g, beta < 0 ? 0 : beta);
+    const int rv = beta < 0 ? 0 : block_rows_valid(g, bc);
+    const int cv = block_cols_valid(g, bc);
+    const int64_t base = hoff + block_base(g, beta, bc);
+#pragma unroll
+    for (int p = 0; p < A::kPasses; ++p) {
+      const int r = ld_row + p * A::kRowsPerPass;
+      if ((r >> 3) < rv && (r & 7) < cv) {
+        const int64_t off = base + (r >> 3) * row_step + (r & 7) * D + ld_chunk * 8;
+        kreg[p] = *(const u32x4*)(K + off);
+        vreg[p] = *(const u32x4*)(V + off);
+      } else {
+        kreg[p] = u32x4{0u, 0u, 0u, 0u};
+        vreg[p] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  // block indices outside [0, nb) are replaced by an all-pad block (never
+  // loaded, all keys masked): a malformed list cannot cause wild reads
+  auto col_at = [&](int idx) {
+    const int c = cols[idx];
+    return (unsigned)c < (unsigned)nb ? c : -1;
+  };
+  if (begin < end) fetch(col_at(begin));
+  for (int idx = begin; idx < end; ++idx) {
+    const int beta = col_at(idx);
+    __syncthreads();                 // every wavefront is done with the previous tile
+#pragma unroll
+    for (int p = 0; p < A::kPasses; ++p) {
+      const int r = ld_row + p * A::kRowsPerPass;
+      *(u32x4*)(Ks + r * A::kStride + ld_chunk * 8) = kreg[p];
+      *(u32x4*)(Vs + r * A::kStride + ld_chunk * 8) = vreg[p];
+    }
+    __syncthreads();
+    if (idx + 1 < end) fetch(col_at(idx + 1));
+
+    // ---- S^T (64 keys x 32 queries) ----
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int s = 0; s < A::kSteps; ++s) {
+        const bf16x8 a = *(const bf16x8*)(Ks + (32 * kt + jl) * A::kStride + 16 * s + 8 * hl);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[s], sacc[kt], 0, 0, 0);
+      }
+    }
+    // element r of sacc[kt] is key 32kt + 8(r/4) + 4hl + (r%4) of this lane's query
+    const BlockCoord bc = block_coord(g, beta < 0 ? 0 : beta);
+    const int rv = beta < 0 ? 0 : block_rows_valid(g, bc);
+    const int cv = block_cols_valid(g, bc);
+    const bool edge = rv < kP || cv < kP;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = sacc[kt][r] * scale_log2;
+        if (edge) {
+          const int key = 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (!((key >> 3) < rv && (key & 7) < cv)) x = -INFINITY;
+        }
+        sacc[kt][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // move the reference only when needed (wavefront-uniform decision)
+    const bool grow = mx > m_run + 8.0f;
+    if (__any(grow)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2f(m_run - m_new);   // 0 on the first block
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < A::kDTiles; ++t) oacc[t] *= alpha;
+      m_run = m_new;
+    }
+    bf16x8 pop[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = exp2f(sacc[kt][8 * h + e] - m_run);
+          l_run += p;
+          pop[kt][h][e] = (__bf16)p;
+        }
+      }
+    }
+    // ---- O^T (d x 32 queries) += V^T P^T ----
+#pragma unroll
+    for (int dt = 0; dt < A::kDTiles; ++dt) {
+      const __bf16* vcol = Vs + 32 * dt + jl;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k0 = 32 * kt + 16 * h + 4 * hl;   // keys k0..k0+3 and k0+8..k0+11
+          bf16x8 a;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[e] = vcol[(k0 + (e < 4 ? e : e + 4)) * A::kStride];
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[kt][h], oacc[dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- normalise and write this lane's query row ----
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (qvalid || g.layout == 1) {
+    __bf16* orow = O + qoff;
+#pragma unroll
+    for (int dt = 0; dt < A::kDTiles; ++dt) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(qvalid ? oacc[dt][4 * gq + e] * inv : 0.f);
+        *(bf16x4*)(orow + 32 * dt + 8 * gq + 4 * hl) = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 path: one thread per query token, fp32 FMA, exact online softmax
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(64)
+attn_fwd_f32_kernel(const Geo g, const float* __restrict__ Q, const float* __restrict__ K,
+                    const float* __restrict__ V, const int32_t* __restrict__ row_ptr,
+                    const int32_t* __restrict__ col_idx, float scale, float* __restrict__ O) {
+  __shared__ __attribute__((aligned(16))) float Kt[kN * D];
+  __shared__ __attribute__((aligned(16))) float Vt[kN * D];
+  const int nb = g.nb;
+  const int64_t head = blockIdx.x / nb;
+  const int qb = (int)(blockIdx.x - head * nb);
+  const int s = threadIdx.x;
+  const int64_t hoff = head * (int64_t)g.head_elems;
+  const int row_step = block_row_step(g);
+  const BlockCoord qc = block_coord(g, qb);
+  const bool qvalid = (s >> 3) < block_rows_valid(g, qc) && (s & 7) < block_cols_valid(g, qc);
+  const int64_t qoff = hoff + block_base(g, qb, qc) + (s >> 3) * row_step + (s & 7) * D;
+
+  float qv[D], acc[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    qv[c] = qvalid ? Q[qoff + c] : 0.f;
+    acc[c] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int32_t* rp = row_ptr + head * (nb + 1);
+  const int32_t* cols = col_idx + head * (int64_t)nb * nb;
+  const int begin = rp[qb];
+  int end = rp[qb + 1];
+  if (begin < 0 || end < begin || end > nb * nb) end = begin;   // malformed row: no keys
+  for (int idx = begin; idx < end; ++idx) {
+    const int beta = cols[idx];
+    if ((unsigned)beta >= (unsigned)nb) continue;               // uniform across the block
+    const BlockCoord bc = block_coord(g, beta);
+    const int rv = block_rows_valid(g, bc), cv = block_cols_valid(g, bc);
+    const int64_t base = hoff + block_base(g, beta, bc);
+    __syncthreads();
+    for (int i = threadIdx.x; i < kN * D / 4; i += 64) {
+      const int r = i / (D / 4), c4 = i % (D / 4);
+      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      if ((r >> 3) < rv && (r & 7) < cv) {
+        const int64_t off = base + (r >> 3) * row_step + (r & 7) * D + 4 * c4;
+        kv = *(const f32x4*)(K + off);
+        vv = *(const f32x4*)(V + off);
+      }
+      *(f32x4*)(Kt + r * D + 4 * c4) = kv;
+      *(f32x4*)(Vt + r * D + 4 * c4) = vv;
+    }
+    __syncthreads();
+    for (int r = 0; r < kN; ++r) {
+      if (!((r >> 3) < rv && (r & 7) < cv)) continue;
+      float dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < D; ++c) dot = fmaf(qv[c], Kt[r * D + c], dot);
+      const float x = dot * scale;
+      const float m_new = fmaxf(m, x);
+      const float corr = expf(m - m_new);
+      const float p = expf(x - m_new);
+      l = l * corr + p;
+#pragma unroll
+      for (int c = 0; c < D; ++c) acc[c] = fmaf(p, Vt[r * D + c], acc[c] * corr);
+      m = m_new;
+    }
+  }
+  if (qvalid || g.layout == 1) {
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+    for (int c = 0; c < D; ++c) O[qoff + c] = qvalid ? acc[c] * inv : 0.f;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const Geo& g, bool bf16, const void* q, const void* k, const void* v,
+                           const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
+                           hipStream_t s) {
+  const int64_t tiles = g.bh * g.nb;
+  if (bf16) {
+    const float sl2 = scale * 1.4426950408889634f;   // softmax in base 2
+    if (g.d == 64) {
+      hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3((unsigned)tiles), dim3(128), 0, s, g,
+                         (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
+                         sl2, (__bf16*)o);
+    } else {
+      hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3((unsigned)tiles), dim3(128), 0, s, g,
+                         (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
+                         sl2, (__bf16*)o);
+    }
+  } else {
+    if (g.d == 64) {
+      hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, dim3((unsigned)tiles), dim3(64), 0, s, g,
+                         (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx,
+                         scale, (float*)o);
+    } else {
+      hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, dim3((unsigned)tiles), dim3(64), 0, s, g,
+                         (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx,
+                         scale, (float*)o);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nabla

@@ -1,0 +1,89 @@
+// Shared device-side definitions of libnabla (gfx950): geometry of the
+// fractal-flattened latent, token addressing in either tensor layout, vector
+// types for the matrix cores, and the internal launcher declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nabla {
+
+constexpr int kP = 8;          // patch side
+constexpr int kN = kP * kP;    // tokens per block
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// Geometry of one call.  Blocks are P x P spatial patches of one frame
+// ("NABLA: Neighborhood Adaptive Block-Level Attention", gist.science,
+// Methodology: token reordering); H and W are padded up to Hp, Wp.
+struct Geo {
+  int64_t bh;        // batch * heads
+  int T, H, W;       // valid extents
+  int gh, gw;        // block rows / columns per frame (Hp / 8, Wp / 8)
+  int nb;            // blocks per head
+  int d;             // head dim
+  int layout;        // 0: [.., T, H, W, d]   1: [.., nb, 64, d]
+  int head_elems;    // elements per head in the tensor layout (< 2^31)
+};
+
+struct BlockCoord {
+  int t, hb, wb;
+};
+
+__host__ __device__ inline BlockCoord block_coord(const Geo& g, int b) {
+  const int per_frame = g.gh * g.gw;
+  BlockCoord c;
+  c.t = b / per_frame;
+  const int r = b - c.t * per_frame;
+  c.hb = r / g.gw;
+  c.wb = r - c.hb * g.gw;
+  return c;
+}
+
+// Valid rows / columns of block b's 8 x 8 patch (8 unless it overhangs the latent edge).
+__device__ inline int block_rows_valid(const Geo& g, const BlockCoord& c) {
+  const int r = g.H - c.hb * kP;
+  return r < kP ? r : kP;
+}
+__device__ inline int block_cols_valid(const Geo& g, const BlockCoord& c) {
+  const int r = g.W - c.wb * kP;
+  return r < kP ? r : kP;
+}
+
+// Element offset (inside one head) of the first token of block b, and the
+// offset step between patch rows; a slot s = i*8 + j of the block sits at
+// base + i * row_step + j * d.  In the natural layout the 8 tokens of a patch
+// row are contiguous and consecutive patch rows are W tokens apart; in the
+// blocked layout the whole block is one contiguous run of 64 tokens.
+__device__ inline int block_base(const Geo& g, int b, const BlockCoord& c) {
+  if (g.layout == 0) return ((c.t * g.H + c.hb * kP) * g.W + c.wb * kP) * g.d;
+  return b * kN * g.d;
+}
+__device__ inline int block_row_step(const Geo& g) {
+  return g.layout == 0 ? g.W * g.d : kP * g.d;
+}
+
+// ---------------------------------------------------------------------------
+// launchers (each returns the hipError_t of its launch)
+// ---------------------------------------------------------------------------
+// forward: src natural -> dst blocked; inverse: src blocked -> dst natural
+hipError_t launch_flatten(const Geo& g, int elem_bytes, const void* src, void* dst, bool inverse,
+                          hipStream_t s);
+hipError_t launch_pool(const Geo& g, bool bf16, const void* q, const void* k, float* qbar,
+                       float* kbar, hipStream_t s);
+hipError_t launch_mask(const Geo& g, const float* qbar, const float* kbar, float thr,
+                       const int sta[3], uint32_t* bits, int32_t* cnt, uint32_t* abits,
+                       hipStream_t s);
+hipError_t launch_compact(const Geo& g, const uint32_t* bits, const int32_t* cnt,
+                          int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
+hipError_t launch_attn_fwd(const Geo& g, bool bf16, const void* q, const void* k, const void* v,
+                           const int32_t* row_ptr, const int32_t* col_idx, float scale,
+                           void* o, hipStream_t s);
+
+}  // namespace nabla

@@ -1,0 +1,191 @@
+/*
+ * nabla.h -- C ABI of libnabla: NABLA (Neighborhood Adaptive Block-Level
+ * Attention) self-attention for AMD Instinct MI355X (gfx950).
+ *
+ * Method sources (pages as titled; sections named):
+ *   [GZ] "NABLA: Neighborhood Adaptive Block-Level Attention", gist.science
+ *        (Chinese), technical summary, section "Methodology: NABLA".
+ *   [LS] lsdiaocha.cn article on NABLA (Sber AI), section 2 (core
+ *        innovations), section 4 (technical principles), section 5
+ *        (comparison with existing techniques).
+ *
+ * One call of the method, in order:
+ *   nabla_flatten     token reordering into P x P patches        [GZ] token reordering
+ *   nabla_pool        average-pool Q and K into block delegates   [GZ] downsampling
+ *   nabla_mask        reduced softmax map, CDF cut, STA union      [GZ] reduced attention,
+ *                                                                  CDF thresholding, hybrid STA
+ *   nabla_compact     per-head compressed (CSR) kept-block lists   [LS] sec. 5
+ *   nabla_attn_fwd    exact attention on kept N x N token blocks   [GZ] expansion; [LS] sec. 2
+ *   nabla_unflatten   inverse reorder of the output
+ *   nabla_forward     pool -> mask -> compact -> attn_fwd in one call
+ *
+ * Conventions for every entry point
+ *   - All pointers except `geom`, `sta` and `bytes`/`offsets` outputs are
+ *     DEVICE pointers, allocated and owned by the caller.  The library
+ *     allocates no memory and keeps no state between calls apart from the
+ *     thread-local last HIP error.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream and returns; it never synchronizes.
+ *   - Return value: NABLA_OK (0) or a negative NABLA_E_* code.  All argument
+ *     checks run before anything is enqueued: a call that returns an error
+ *     has launched nothing.  A failed launch returns NABLA_E_HIP and keeps the
+ *     hipError_t for nabla_last_hip_error().  No call aborts or throws.
+ *   - batch == 0 or heads == 0 is a valid empty call: NABLA_OK, no launch.
+ *
+ * Geometry and layouts
+ *   The latent is T x H x W tokens (valid extents).  Blocks are P x P spatial
+ *   patches of one frame, P = 8, so a block holds N = P*P = 64 tokens.
+ *   H and W are padded up to Hp, Wp (multiples of P); the block grid is
+ *   T x (Hp/P) x (Wp/P) and nb = T * (Hp/P) * (Wp/P).  Block b has frame
+ *   t = b / ((Hp/P)(Wp/P)), block row hb and block column wb (row-major);
+ *   slot s of the block is patch row s / P and patch column s % P.
+ *
+ *   NABLA_LAYOUT_THW:     tensor [B, heads, T, H, W, d]  (natural order,
+ *                         valid tokens only; the reorder is applied inside
+ *                         the kernels' address computation)
+ *   NABLA_LAYOUT_BLOCKED: tensor [B, heads, nb, 64, d]   (already flattened;
+ *                         pad slots present in memory and ignored on input)
+ *   Q, K, V and O of one call share one layout and dtype, contiguous.
+ *   Pooled tensors qbar, kbar: float32 [B, heads, nb, d].
+ *   Masks: uint32 [B, heads, nb, nw], nw = ceil(nb / 32); block c of row r is
+ *   kept iff bit (c % 32) of word (c / 32) is set.  Bits >= nb are zero.
+ *   Row counts: int32 [B, heads, nb].
+ *   CSR: row_ptr int32 [B*heads, nb + 1] (offsets inside that head's list);
+ *        col_idx int32 [B*heads, nb * nb] capacity; head i's list starts at
+ *        col_idx + i * nb * nb; kept block indices of a row are ascending.
+ */
+#ifndef NABLA_H
+#define NABLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NABLA_ABI_VERSION 1
+
+enum nabla_status {
+  NABLA_OK = 0,
+  NABLA_E_NULL = -1,        /* a required pointer is NULL */
+  NABLA_E_SHAPE = -2,       /* batch/heads < 0, T/H/W < 1, or sizes overflow the limits */
+  NABLA_E_DTYPE = -3,       /* dtype not NABLA_DTYPE_F32 / NABLA_DTYPE_BF16 */
+  NABLA_E_HEAD_DIM = -4,    /* head_dim not 64 or 128 */
+  NABLA_E_PATCH = -5,       /* P != 8 */
+  NABLA_E_THR = -6,         /* thr not in (0, 1] or not finite */
+  NABLA_E_STA = -7,         /* STA window not all-zero or all positive odd */
+  NABLA_E_WORKSPACE = -8,   /* workspace smaller than nabla_forward_workspace_size */
+  NABLA_E_LAYOUT = -9,      /* layout not NABLA_LAYOUT_THW / NABLA_LAYOUT_BLOCKED */
+  NABLA_E_HIP = -10,        /* a HIP launch failed; see nabla_last_hip_error() */
+  NABLA_E_SCALE = -11,      /* softmax scale not finite and > 0 */
+  NABLA_E_TOO_LARGE = -12   /* nb above NABLA_MAX_BLOCKS */
+};
+
+enum nabla_dtype { NABLA_DTYPE_F32 = 0, NABLA_DTYPE_BF16 = 1 };
+enum nabla_layout { NABLA_LAYOUT_THW = 0, NABLA_LAYOUT_BLOCKED = 1 };
+
+/* Largest number of blocks per head (the mask kernel keeps one row of
+ * nb scores in registers across a wavefront). */
+#define NABLA_MAX_BLOCKS 4096
+
+typedef struct nabla_geom {
+  int64_t batch;     /* B >= 0 */
+  int64_t heads;     /* heads >= 0 */
+  int32_t T, H, W;   /* valid latent extents, each >= 1 */
+  int32_t P;         /* patch side; must be 8 */
+  int32_t head_dim;  /* d: 64 or 128 */
+  int32_t dtype;     /* enum nabla_dtype: element type of Q, K, V, O */
+  int32_t layout;    /* enum nabla_layout: layout of Q, K, V, O */
+} nabla_geom;
+
+/* Number of blocks per head, nb (see Geometry above). */
+int nabla_num_blocks(const nabla_geom* geom, int64_t* nb);
+
+/* Fractal flatten ([GZ] Methodology, token reordering): every P x P spatial
+ * patch of a frame becomes one contiguous run of 64 tokens, patches in
+ * row-major order over the frame, frames in temporal order.
+ * x: [B, heads, T, H, W, d] (geom->layout is ignored) -> x_blocked:
+ * [B, heads, nb, 64, d]; pad slots are written as zeros.  Bit-exact copy. */
+int nabla_flatten(const nabla_geom* geom, const void* x, void* x_blocked, void* stream);
+
+/* Inverse of nabla_flatten on valid slots: [B, heads, nb, 64, d] ->
+ * [B, heads, T, H, W, d].  Bit-exact copy. */
+int nabla_unflatten(const nabla_geom* geom, const void* x_blocked, void* x, void* stream);
+
+/* Block average pooling of Q and K ([GZ] Methodology, downsampling;
+ * [LS] sec. 2 and 4): qbar[b, h, c, :] = mean of the valid tokens of block c,
+ * accumulated in float32.  q, k in geom's layout and dtype; qbar, kbar
+ * float32 [B, heads, nb, d]. */
+int nabla_pool(const nabla_geom* geom, const void* q, const void* k,
+               float* qbar, float* kbar, void* stream);
+
+/* Adaptive block mask ([GZ] Methodology, reduced attention + CDF
+ * thresholding + hybrid integration with STA).  For every row r of every
+ * head: s_c = qbar_r . kbar_c * (1 / sqrt(d)) in float32, p = softmax(s);
+ * the kept set is the smallest set of blocks taken in order of decreasing p
+ * (ties: lower block index first) whose total probability reaches thr
+ * (thr = 1 keeps every block).  If sta = {wt, wh, ww} is non-zero, every
+ * block within wt/2 frames, wh/2 block rows and ww/2 block columns of the
+ * row's own block is added (window clipped at the borders).
+ *   thr            in (0, 1]
+ *   sta            host array of 3 ints; NULL or {0,0,0} = no STA;
+ *                  otherwise three positive odd numbers
+ *   mask_bits      out, uint32 [B, heads, nb, nw]: union mask
+ *   row_count      out, int32 [B, heads, nb]: kept blocks per row (union)
+ *   adaptive_bits  optional out (may be NULL), uint32 [B, heads, nb, nw]:
+ *                  the CDF-threshold mask before the STA union */
+int nabla_mask(const nabla_geom* geom, const float* qbar, const float* kbar,
+               float thr, const int32_t* sta, uint32_t* mask_bits,
+               int32_t* row_count, uint32_t* adaptive_bits, void* stream);
+
+/* Compressed kept-block lists ([LS] sec. 5, storing only the compressed
+ * sparse matrix): per head, row_ptr = exclusive prefix sum of row_count and
+ * col_idx = the kept block indices of each row in ascending order.
+ * mask_bits, row_count as produced by nabla_mask; row_ptr int32
+ * [B*heads, nb + 1]; col_idx int32 with capacity B*heads*nb*nb. */
+int nabla_compact(const nabla_geom* geom, const uint32_t* mask_bits,
+                  const int32_t* row_count, int32_t* row_ptr, int32_t* col_idx,
+                  void* stream);
+
+/* Block-sparse attention forward ([GZ] Methodology, expansion of the block
+ * mask to token resolution; [LS] sec. 2, step 3): for each valid query token
+ * i of block r, o_i = sum_j softmax_j(q_i . k_j * scale) v_j over the valid
+ * key tokens j of the kept blocks listed for row r.  bf16 inputs use bf16
+ * matrix cores with float32 accumulation and a float32 online softmax;
+ * float32 inputs compute in float32.  q, k, v, o in geom's layout and dtype;
+ * in NABLA_LAYOUT_BLOCKED pad query slots of o are written as zeros.  A row
+ * with an empty list produces zeros.  scale > 0 (usually 1/sqrt(d)).
+ * col_idx entries must lie in [0, nb). */
+int nabla_attn_fwd(const nabla_geom* geom, const void* q, const void* k,
+                   const void* v, const int32_t* row_ptr, const int32_t* col_idx,
+                   float scale, void* o, void* stream);
+
+/* Workspace for nabla_forward and the byte offsets of its parts, in order:
+ * offsets[0] qbar, [1] kbar, [2] mask_bits, [3] row_count, [4] row_ptr,
+ * [5] col_idx (see the layouts above); `offsets` (host, 6 entries) may be
+ * NULL.  Every part is 256-byte aligned. */
+int nabla_forward_workspace_size(const nabla_geom* geom, size_t* bytes, size_t* offsets);
+
+/* One NABLA attention call: nabla_pool, nabla_mask, nabla_compact and
+ * nabla_attn_fwd in sequence on `stream`, with the intermediates in
+ * `workspace` (device memory of at least nabla_forward_workspace_size bytes,
+ * caller-owned; its parts can be read back after the call). */
+int nabla_forward(const nabla_geom* geom, const void* q, const void* k, const void* v,
+                  float thr, const int32_t* sta, float scale, void* o,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* nabla_status_string(int status);
+
+/* hipError_t of the last failed launch in this thread (0 if none). */
+int nabla_last_hip_error(void);
+
+/* NABLA_ABI_VERSION of the library. */
+int nabla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NABLA_H */

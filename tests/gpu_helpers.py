@@ -1,0 +1,112 @@
+"""Shared helpers of the GPU parity tests (HIP path vs the float64 oracle)."""
+from __future__ import annotations
+
+import math
+import sys
+import time
+
+import numpy as np
+import torch
+
+import block_sparse_attention_flatten_amd as nabla
+import oracle as O
+import synth
+
+# tolerances fixed for bf16 inputs against the float64 oracle; float32 inputs
+# are held to a bound derived from fp32 accumulation over a few thousand keys
+BF16_MAX_ABS, BF16_MEAN_ABS = 1e-2, 1e-3
+F32_MAX_ABS, F32_MEAN_ABS = 2e-5, 2e-6
+BAND_EPS = 1e-5
+
+
+def log(msg: str) -> None:
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def geom_of(cfg: synth.Config, layout=nabla.LAYOUT_THW) -> nabla.Geometry:
+    return nabla.Geometry(cfg.batch, cfg.heads, cfg.T, cfg.H, cfg.W, cfg.head_dim,
+                          cfg.torch_dtype, layout)
+
+
+def ogeom(cfg: synth.Config) -> O.Geometry:
+    return O.Geometry(cfg.T, cfg.H, cfg.W, cfg.P)
+
+
+def unpack_bits(words: torch.Tensor, nb: int) -> np.ndarray:
+    """int32 words [..., nb, nw] -> bool [..., nb, nb]."""
+    w = words.cpu().numpy().view(np.uint32)
+    bits = np.unpackbits(w.view(np.uint8), axis=-1, bitorder="little")
+    return bits[..., :nb].astype(bool)
+
+
+def f64(x: torch.Tensor) -> np.ndarray:
+    return x.detach().to(torch.float64).cpu().numpy()
+
+
+def tol(dtype: torch.dtype):
+    return (BF16_MAX_ABS, BF16_MEAN_ABS) if dtype == torch.bfloat16 else (F32_MAX_ABS, F32_MEAN_ABS)
+
+
+def run_pipeline(cfg: synth.Config, q, k, v, layout=nabla.LAYOUT_THW, thr=None, sta=None):
+    """Run pool -> mask -> compact -> attn through the C ABI, one entry point
+    at a time (the launch sequence bench.py times)."""
+    g = geom_of(cfg, layout)
+    thr = cfg.thr if thr is None else thr
+    sta = cfg.sta if sta is None else sta
+    dev = q.device
+    B, h, nb, d = cfg.batch, cfg.heads, g.nb, cfg.head_dim
+    qbar = torch.empty((B, h, nb, d), dtype=torch.float32, device=dev)
+    kbar = torch.empty_like(qbar)
+    bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
+    abits = torch.empty_like(bits)
+    cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)
+    rp = torch.empty((B * h, nb + 1), dtype=torch.int32, device=dev)
+    ci = torch.empty((B * h, nb * nb), dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    nabla.nabla_pool(g, q, k, qbar, kbar)
+    nabla.nabla_mask(g, qbar, kbar, thr, sta, bits, cnt, abits)
+    nabla.nabla_compact(g, bits, cnt, rp, ci)
+    nabla.nabla_attn_fwd(g, q, k, v, rp, ci, 1.0 / math.sqrt(d), o)
+    torch.cuda.synchronize()
+    return dict(g=g, qbar=qbar, kbar=kbar, bits=bits, abits=abits, cnt=cnt, rp=rp, ci=ci, o=o)
+
+
+def oracle_mask(cfg: synth.Config, q_h: np.ndarray, k_h: np.ndarray, thr=None, sta=None):
+    """Oracle pooling + mask for one head ([T, H, W, d] float64 inputs)."""
+    g = ogeom(cfg)
+    valid = O.valid_tokens(g)
+    qbar = O.pool(O.flatten(q_h, g), valid)
+    kbar = O.pool(O.flatten(k_h, g), valid)
+    thr = cfg.thr if thr is None else thr
+    sta = cfg.sta if sta is None else sta
+    m, m_ad, p = O.nabla_mask(qbar, kbar, thr, g, sta)
+    band_a, band_b = O.band_rows(p, m_ad, thr, BAND_EPS)
+    return dict(qbar=qbar, kbar=kbar, mask=m, mask_adaptive=m_ad, p=p, band=band_a | band_b,
+                band_a=band_a, band_b=band_b, valid=valid)
+
+
+def check_mask_rows(got_union, got_adapt, ref, thr, label=""):
+    """Masks must agree bit for bit outside band rows.  On band rows that
+    differ, the GPU's adaptive set must still be a valid cut under the
+    oracle's probabilities to within the band.  Returns (#band rows, #differing)."""
+    p = ref["p"]
+    diff = (got_adapt != ref["mask_adaptive"]).any(1) | (got_union != ref["mask"]).any(1)
+    bad = diff & ~ref["band"]
+    assert not bad.any(), (f"{label}: mask differs outside the band on rows "
+                           f"{np.flatnonzero(bad)[:10].tolist()}")
+    for r in np.flatnonzero(diff):
+        keep = got_adapt[r]
+        mass = p[r][keep].sum()
+        assert keep.any() and mass >= thr - BAND_EPS, (label, r, mass)
+        assert mass - p[r][keep].min() < thr + BAND_EPS, (label, r)
+    return int(ref["band"].sum()), int(diff.sum())
+
+
+def check_output(got: np.ndarray, ref: np.ndarray, dtype, label=""):
+    max_abs, mean_abs = tol(dtype)
+    err = np.abs(got - ref)
+    assert np.isfinite(got).all(), f"{label}: non-finite output"
+    assert err.max() <= max_abs and err.mean() <= mean_abs, (
+        f"{label}: max|err| {err.max():.3e} mean|err| {err.mean():.3e}")
+    return float(err.max()), float(err.mean())

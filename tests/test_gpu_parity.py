@@ -1,0 +1,235 @@
+"""GPU parity, small and ragged workloads: every kernel of the HIP path
+against the float64 oracle on the same seeded inputs, element by element."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_flatten_amd as nabla
+import oracle as O
+import synth
+from gpu_helpers import (check_mask_rows, check_output, f64, geom_of, log, ogeom,
+                         oracle_mask, run_pipeline, unpack_bits)
+
+pytestmark = pytest.mark.gpu
+
+# (name, config overrides): full Tiny and Small configs, plus ragged latents
+# (H, W not multiples of 8, W < 8), batch > 1, d = 64 in bf16, a one-block latent
+CASES = {
+    "tiny": ("tiny", {}),
+    "small": ("small", {}),
+    "ragged_bf16": ("small", dict(batch=2, heads=3, T=3, H=13, W=21, thr=0.6, sta=(1, 3, 3))),
+    "ragged_f32": ("tiny", dict(batch=2, heads=2, T=2, H=11, W=17, head_dim=128, thr=0.7,
+                                sta=(3, 3, 3))),
+    "narrow": ("small", dict(heads=2, T=4, H=5, W=3, thr=0.5)),
+    "one_block": ("small", dict(heads=2, T=1, H=8, W=8, thr=0.5)),
+    "d64_bf16": ("small", dict(heads=2, T=4, H=24, W=40, head_dim=64, thr=0.8, sta=(3, 3, 3))),
+    "thr_one": ("small", dict(heads=2, T=2, H=16, W=24, thr=1.0)),
+    "thr_low": ("small", dict(heads=2, T=3, H=24, W=24, thr=0.05)),
+}
+
+
+def _cfg(name):
+    base, kw = CASES[name]
+    return synth.config(base, **kw)
+
+
+@pytest.fixture(scope="module", params=sorted(CASES))
+def case(request):
+    name = request.param
+    cfg = _cfg(name)
+    log(f"case {name}: {cfg}")
+    q, k, v = synth.make_qkv(cfg, device="cuda")
+    return name, cfg, q, k, v
+
+
+def test_flatten_bit_exact(case):
+    name, cfg, q, _, _ = case
+    g = geom_of(cfg)
+    xb = torch.full(g.tensor_shape(nabla.LAYOUT_BLOCKED), 7.0, dtype=q.dtype, device="cuda")
+    nabla.nabla_flatten(g, q, xb)
+    back = torch.full_like(q, 3.0)
+    nabla.nabla_unflatten(g, xb, back)
+    torch.cuda.synchronize()
+    og = ogeom(cfg)
+    ref = O.flatten(q.cpu().view(torch.int16 if q.dtype == torch.bfloat16 else torch.int32)
+                    .numpy(), og)
+    got = xb.cpu().view(torch.int16 if q.dtype == torch.bfloat16 else torch.int32).numpy()
+    assert np.array_equal(got, ref), f"{name}: flatten differs"
+    assert torch.equal(back.view(torch.int16 if q.dtype == torch.bfloat16 else torch.int32),
+                       q.view(torch.int16 if q.dtype == torch.bfloat16 else torch.int32))
+
+
+@pytest.mark.parametrize("layout", [nabla.LAYOUT_THW, nabla.LAYOUT_BLOCKED])
+def test_pool(case, layout):
+    name, cfg, q, k, _ = case
+    g = geom_of(cfg, layout)
+    if layout == nabla.LAYOUT_BLOCKED:
+        qi = torch.empty(g.tensor_shape(), dtype=q.dtype, device="cuda")
+        ki = torch.empty_like(qi)
+        nabla.nabla_flatten(g, q, qi)
+        nabla.nabla_flatten(g, k, ki)
+    else:
+        qi, ki = q, k
+    qbar = torch.empty((cfg.batch, cfg.heads, g.nb, cfg.head_dim), device="cuda")
+    kbar = torch.empty_like(qbar)
+    nabla.nabla_pool(g, qi, ki, qbar, kbar)
+    torch.cuda.synchronize()
+    og = ogeom(cfg)
+    valid = O.valid_tokens(og)
+    for x, xbar in ((q, qbar), (k, kbar)):
+        ref = O.pool(O.flatten(f64(x), og), valid)
+        got = f64(xbar)
+        bound = 64 * 2.0 ** -24 * np.abs(f64(x)).max() + 1e-30
+        assert np.abs(got - ref).max() <= bound, (name, np.abs(got - ref).max(), bound)
+
+
+def test_mask_and_forward(case):
+    """pool -> mask -> compact -> attention through the C ABI vs the oracle."""
+    name, cfg, q, k, v = case
+    res = run_pipeline(cfg, q, k, v)
+    g = res["g"]
+    nb = g.nb
+    union = unpack_bits(res["bits"], nb)
+    adapt = unpack_bits(res["abits"], nb)
+    rp = res["rp"].cpu().numpy()
+    ci = res["ci"].cpu().numpy()
+    cnt = res["cnt"].cpu().numpy()
+    og = ogeom(cfg)
+    n_band = n_diff = 0
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            qh, kh, vh = f64(q[b, h]), f64(k[b, h]), f64(v[b, h])
+            ref = oracle_mask(cfg, qh, kh)
+            nbnd, ndf = check_mask_rows(union[b, h], adapt[b, h], ref, cfg.thr, f"{name} b{b} h{h}")
+            n_band += nbnd
+            n_diff += ndf
+            # row counts and CSR describe the GPU's own mask exactly
+            bh = b * cfg.heads + h
+            assert np.array_equal(cnt[b, h], union[b, h].sum(1))
+            assert rp[bh, 0] == 0 and np.array_equal(np.diff(rp[bh]), cnt[b, h])
+            for r in range(nb):
+                cols = ci[bh, rp[bh, r]:rp[bh, r + 1]]
+                assert np.array_equal(cols, np.flatnonzero(union[b, h, r])), (name, b, h, r)
+            # output: rows whose mask matches the oracle's, vs the oracle's attention
+            same = ~(union[b, h] != ref["mask"]).any(1)
+            rows = np.flatnonzero(same)
+            ob = O.block_sparse_attention(O.flatten(qh, og), O.flatten(kh, og), O.flatten(vh, og),
+                                          ref["mask"], ref["valid"], rows=rows)
+            got = O.flatten(f64(res["o"][b, h]), og)
+            sel = np.zeros_like(ref["valid"])
+            sel[rows] = ref["valid"][rows]
+            e = check_output(got[sel], ob[sel], cfg.torch_dtype, f"{name} b{b} h{h}")
+            log(f"{name} b{b} h{h}: kept {union[b, h].mean():.3f} band {nbnd} "
+                f"diff {ndf} max|err| {e[0]:.2e} mean|err| {e[1]:.2e}")
+    log(f"{name}: band rows {n_band}, differing rows {n_diff}")
+
+
+def test_attention_with_oracle_masks(case):
+    """Attention kernel alone, fed the oracle's mask (and random masks with
+    one-block, empty-ish and full rows) as CSR."""
+    name, cfg, q, k, v = case
+    g = geom_of(cfg)
+    og = ogeom(cfg)
+    nb = g.nb
+    rng = np.random.default_rng(11)
+    masks = []
+    for b in range(cfg.batch):
+        row = []
+        for h in range(cfg.heads):
+            m = rng.random((nb, nb)) < 0.3
+            m[np.arange(nb), rng.integers(0, nb, nb)] = True   # >= 1 per row
+            if nb > 2:
+                m[0] = True                                     # a full row
+                m[1] = False
+                m[1, nb - 1] = True                             # a one-block row
+            row.append(m)
+        masks.append(row)
+    rp = np.zeros((cfg.batch * cfg.heads, nb + 1), np.int32)
+    ci = np.zeros((cfg.batch * cfg.heads, nb * nb), np.int32)
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            p_, c_ = O.to_csr(masks[b][h])
+            rp[b * cfg.heads + h] = p_
+            ci[b * cfg.heads + h, :len(c_)] = c_
+    o = torch.empty_like(q)
+    nabla.nabla_attn_fwd(g, q, k, v, torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda(),
+                         1.0 / math.sqrt(cfg.head_dim), o)
+    torch.cuda.synchronize()
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            ob = O.block_sparse_attention(O.flatten(f64(q[b, h]), og), O.flatten(f64(k[b, h]), og),
+                                          O.flatten(f64(v[b, h]), og), masks[b][h],
+                                          O.valid_tokens(og))
+            got = O.unflatten(ob, og)
+            check_output(f64(o[b, h]), got, cfg.torch_dtype, f"{name} random-mask b{b} h{h}")
+
+
+def test_compact_against_oracle_csr():
+    """Compaction alone: random masks (some empty and full rows) -> CSR, bit-exact."""
+    cfg = synth.config("small", batch=2, heads=3, T=5, H=24, W=40)
+    g = geom_of(cfg)
+    nb = g.nb
+    rng = np.random.default_rng(5)
+    m = rng.random((cfg.batch, cfg.heads, nb, nb)) < rng.random((1, 1, nb, 1))
+    m[0, 0, 3] = False
+    m[0, 1, 4] = True
+    words = np.packbits(np.pad(m, [(0, 0)] * 3 + [(0, g.nw * 32 - nb)]), axis=-1,
+                        bitorder="little").view(np.uint32).view(np.int32)
+    bits = torch.from_numpy(np.ascontiguousarray(words)).cuda()
+    cnt = torch.from_numpy(m.sum(-1).astype(np.int32)).cuda()
+    rp = torch.full((cfg.batch * cfg.heads, nb + 1), -1, dtype=torch.int32, device="cuda")
+    ci = torch.full((cfg.batch * cfg.heads, nb * nb), -1, dtype=torch.int32, device="cuda")
+    nabla.nabla_compact(g, bits, cnt, rp, ci)
+    torch.cuda.synchronize()
+    rp, ci = rp.cpu().numpy(), ci.cpu().numpy()
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            p_, c_ = O.to_csr(m[b, h])
+            i = b * cfg.heads + h
+            assert np.array_equal(rp[i], p_)
+            assert np.array_equal(ci[i, :len(c_)], c_)
+            assert np.all(ci[i, len(c_):] == -1)
+
+
+def test_forward_entry_point_matches_stepwise():
+    """nabla_forward (one call) == the four entry points called one by one, bit for bit."""
+    cfg = synth.config("small", heads=3, T=3, H=21, W=30, thr=0.75, sta=(3, 3, 3))
+    q, k, v = synth.make_qkv(cfg, device="cuda")
+    step = run_pipeline(cfg, q, k, v)
+    res = nabla.forward(q, k, v, cfg.thr, cfg.sta)
+    torch.cuda.synchronize()
+    assert torch.equal(res.o.view(torch.int16), step["o"].view(torch.int16))
+    assert torch.equal(res.mask_bits, step["bits"])
+    assert torch.equal(res.row_ptr, step["rp"])
+
+
+def test_blocked_layout_forward_matches_thw():
+    cfg = synth.config("small", heads=2, T=3, H=19, W=27, thr=0.7, sta=(3, 3, 3))
+    q, k, v = synth.make_qkv(cfg, device="cuda")
+    g = geom_of(cfg)
+    blk = [torch.empty(g.tensor_shape(nabla.LAYOUT_BLOCKED), dtype=q.dtype, device="cuda")
+           for _ in range(3)]
+    for x, xb in zip((q, k, v), blk):
+        nabla.nabla_flatten(g, x, xb)
+    r_thw = nabla.forward(q, k, v, cfg.thr, cfg.sta)
+    r_blk = nabla.forward(*blk, cfg.thr, cfg.sta, layout=nabla.LAYOUT_BLOCKED, T=cfg.T, H=cfg.H,
+                          W=cfg.W)
+    back = torch.empty_like(q)
+    nabla.nabla_unflatten(g, r_blk.o, back)
+    torch.cuda.synchronize()
+    assert torch.equal(r_thw.mask_bits, r_blk.mask_bits)
+    assert torch.equal(back.view(torch.int16), r_thw.o.view(torch.int16))
+    # pad query slots of the blocked output are zero
+    valid = torch.from_numpy(O.valid_tokens(ogeom(cfg))).cuda()
+    assert (r_blk.o[:, :, ~valid] == 0).all()
+
+
+def test_empty_batch_is_a_no_op():
+    cfg = synth.config("small", batch=0, heads=4, T=2, H=16, W=16)
+    g = geom_of(cfg)
+    q = torch.empty(g.tensor_shape(), dtype=torch.bfloat16, device="cuda")
+    res = nabla.forward(q, q, q, 0.5, (3, 3, 3))
+    torch.cuda.synchronize()
+    assert res.o.numel() == 0
