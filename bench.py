@@ -1,0 +1,277 @@
+"""Benchmark of one NABLA attention call on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 720p]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+nabla_pool -> nabla_mask -> nabla_compact -> nabla_attn_fwd, called through
+the C ABI on torch's current stream, with the fractal flatten applied inside
+the pooling and attention loaders (inputs and output stay in the natural
+[B, heads, T, H, W, d] layout).  Inputs are resident in HBM before timing.
+Prints ONE JSON line (plus progress on stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NABLA attn ms/call + effective TFLOP/s (kept blocks) at 720p Wan-shape, 1 GPU"
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
+
+WORKLOAD_NAMES = {
+    "tiny": "Tiny NABLA attention (1x2 heads, d=64, fp32, 4x16x16)",
+    "small": "Small NABLA attention (1x8 heads, d=128, bf16, 8x32x32)",
+    "480p": "Wan-2.1-14B-shaped 480p NABLA attention layer (40 heads, d=128, 21x30x52)",
+    "720p": "Wan-2.1-14B-shaped 720p NABLA attention layer (40 heads, d=128, 21x45x80)",
+    "long": "Long 720p NABLA attention layer (40 heads, d=128, 41x45x80)",
+}
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="720p", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--thr", type=float, default=None)
+    ap.add_argument("--sta", type=str, default=None, help="e.g. 3,3,3 or 0,0,0")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(cfg, nb, nnz_total):
+    """HBM bytes each mask-construction stage must move at minimum."""
+    bh = cfg.batch * cfg.heads
+    es = 2 if cfg.dtype == "bf16" else 4
+    d = cfg.head_dim
+    nw = -(-nb // 32)
+    tokens = cfg.T * cfg.H * cfg.W
+    pool = 2 * bh * tokens * d * es + 2 * bh * nb * d * 4
+    mask = 2 * bh * nb * d * 4 + bh * nb * nw * 4 + bh * nb * 4
+    compact = bh * nb * nw * 4 + bh * nb * 4 + bh * (nb + 1) * 4 + nnz_total * 4
+    return pool, mask, compact
+
+
+def cpu_baseline(cfg, q, k, v, thr, sta, budget_s):
+    """Time the float64 oracle on a bounded sample of the same workload: one
+    head's full mask construction plus attention for as many query blocks as
+    fit in the time budget, extrapolated to the whole call."""
+    import numpy as np
+    import oracle as O
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    g = O.Geometry(cfg.T, cfg.H, cfg.W, cfg.P)
+    h = 0
+    qh = q[0, h].double().cpu().numpy()
+    kh = k[0, h].double().cpu().numpy()
+    vh = v[0, h].double().cpu().numpy()
+    t0 = time.perf_counter()
+    valid = O.valid_tokens(g)
+    qb, kb, vb = O.flatten(qh, g), O.flatten(kh, g), O.flatten(vh, g)
+    m, _, _ = O.nabla_mask(O.pool(qb, valid), O.pool(kb, valid), thr, g, sta)
+    t_mask = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    order = rng.permutation(g.nb)
+    done, t_attn, kept_pairs = 0, 0.0, 0
+    while done < g.nb and t_mask + t_attn < budget_s:
+        rows = order[done:done + 16]
+        t1 = time.perf_counter()
+        O.block_sparse_attention(qb, kb, vb, m, valid, rows=rows)
+        t_attn += time.perf_counter() - t1
+        kept_pairs += int(m[rows].sum())
+        done += len(rows)
+    per_head = t_mask + t_attn * g.nb / done
+    seconds = per_head * cfg.heads * cfg.batch
+    flops_head = int(m.sum()) * 4 * 64 * 64 * cfg.head_dim
+    return {
+        "value": flops_head * cfg.heads * cfg.batch / seconds / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"float64 oracle, head 0 of {cfg.heads}: full mask construction "
+                   f"({g.nb} rows) + attention for {done} of {g.nb} query blocks "
+                   f"({t_mask + t_attn:.1f} s CPU); extrapolated to the whole call "
+                   f"= {seconds:.0f} s"),
+        "seconds_per_call_extrapolated": seconds,
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the NABLA call "
+              "shards by head with no communication, so run it per GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_flatten_amd as nabla
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = synth.config(args.config)
+    thr = cfg.thr if args.thr is None else args.thr
+    sta = cfg.sta if args.sta is None else tuple(int(x) for x in args.sta.split(","))
+    log(f"config {cfg.name}: {cfg} thr={thr} sta={sta}")
+    q, k, v = synth.make_qkv(cfg, device="cuda")
+    torch.cuda.synchronize()
+
+    g = nabla.Geometry(cfg.batch, cfg.heads, cfg.T, cfg.H, cfg.W, cfg.head_dim, cfg.torch_dtype)
+    B, h, nb, d = cfg.batch, cfg.heads, g.nb, cfg.head_dim
+    dev = q.device
+    qbar = torch.empty((B, h, nb, d), dtype=torch.float32, device=dev)
+    kbar = torch.empty_like(qbar)
+    bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)
+    rp = torch.empty((B * h, nb + 1), dtype=torch.int32, device=dev)
+    ci = torch.empty((B * h, nb * nb), dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(d)
+    stream = torch.cuda.current_stream()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+
+    def step(marks=None):
+        if marks is not None:
+            marks[0].record(stream)
+        nabla.nabla_pool(g, q, k, qbar, kbar, stream)
+        nabla.nabla_mask(g, qbar, kbar, thr, sta, bits, cnt, None, stream)
+        nabla.nabla_compact(g, bits, cnt, rp, ci, stream)
+        if marks is not None:
+            marks[1].record(stream)
+        nabla.nabla_attn_fwd(g, q, k, v, rp, ci, scale, o, stream)
+        if marks is not None:
+            marks[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    marks = [[ev(), ev(), ev()] for _ in range(args.steps)]
+    t_start, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(marks[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    mask_ms = sorted(m[0].elapsed_time(m[1]) for m in marks)
+    attn_ms = sorted(m[1].elapsed_time(m[2]) for m in marks)
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    mask_avg = sum(mask_ms) / len(mask_ms)
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (mask {mask_avg:.3f}, "
+        f"attn {attn_avg:.3f})")
+
+    # per-stage breakdown (separate, untimed-region runs) and the explicit reorder
+    def time_call(fn, reps=5):
+        a, b = ev(), ev()
+        fn()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    xb = torch.empty(g.tensor_shape(nabla.LAYOUT_BLOCKED), dtype=q.dtype, device=dev)
+    stages = {
+        "pool": time_call(lambda: nabla.nabla_pool(g, q, k, qbar, kbar, stream)),
+        "mask": time_call(lambda: nabla.nabla_mask(g, qbar, kbar, thr, sta, bits, cnt, None,
+                                                   stream)),
+        "compact": time_call(lambda: nabla.nabla_compact(g, bits, cnt, rp, ci, stream)),
+        "attn_fwd": attn_avg,
+        "flatten_one_tensor": time_call(lambda: nabla.nabla_flatten(g, q, xb, stream)),
+        "unflatten_one_tensor": time_call(lambda: nabla.nabla_unflatten(g, xb, o, stream)),
+    }
+    # restore o (the unflatten timing overwrote it) and measure the mask statistics
+    step()
+    torch.cuda.synchronize()
+    counts = cnt.to(torch.int64)
+    nnz = int(counts.sum())
+    kept_flops = nnz * 4 * 64 * 64 * d
+    sparsity = 1.0 - nnz / (B * h * nb * nb)
+    per_row = counts.flatten().float()
+    pool_b, mask_b, compact_b = algorithmic_bytes(cfg, nb, nnz)
+    mc_bytes = pool_b + mask_b + compact_b
+    mc_ms = stages["pool"] + stages["mask"] + stages["compact"]
+
+    attn_tflops = kept_flops / (attn_avg * 1e-3) / 1e12
+    value = kept_flops / (ms_per_step * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded smooth spatio-temporal fields + noise; no weights)",
+        "config": {
+            "workload": WORKLOAD_NAMES[cfg.name],
+            "batch": B, "heads": h, "head_dim": d, "latent_THW": [cfg.T, cfg.H, cfg.W],
+            "patch": cfg.P, "blocks_per_head": nb, "tokens_padded": nb * 64,
+            "thr": thr, "sta": list(sta),
+        },
+        "roofline": {
+            "kernel": "nabla_attn_fwd (attn_fwd_bf16_kernel)",
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "work_per_launch": f"{nnz} kept 64x64 block pairs x 4*64*64*{d} flop = "
+                               f"{kept_flops / 1e12:.3f} TFLOP",
+            "avg_launch_ms": round(attn_avg, 4),
+        },
+        "mask_construction": {
+            "bound": "hbm",
+            "ms": round(mc_ms, 4),
+            "algorithmic_bytes": mc_bytes,
+            "achieved": round(mc_bytes / (mc_ms * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(mc_bytes / (mc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "stages_ms": {k_: round(v_, 4) for k_, v_ in stages.items()},
+        "attn_ms_min_median": [round(attn_ms[0], 4), round(attn_ms[len(attn_ms) // 2], 4)],
+        "sparsity": round(sparsity, 4),
+        "kept_per_row_min_mean_max": [int(per_row.min()), round(float(per_row.mean()), 1),
+                                      int(per_row.max())],
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, thr, sta, args.cpu_seconds)
+        log(f"cpu baseline done: {result['cpu_baseline']['value']:.6f} TFLOP/s")
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

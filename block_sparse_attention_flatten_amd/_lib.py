@@ -29,7 +29,7 @@ class nabla_geom(ctypes.Structure):
         ("batch", ctypes.c_int64), ("heads", ctypes.c_int64),
         ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32),
         ("P", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-        ("dtype", ctypes.c_int32), ("layout", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("layout", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
     ]
 
 

@@ -61,6 +61,11 @@ class Geometry:
     dtype: torch.dtype
     layout: int = LAYOUT_THW
     P: int = 8
+    out_dtype: Optional[torch.dtype] = None   # dtype of O; None = dtype
+
+    @property
+    def odtype(self) -> torch.dtype:
+        return self.dtype if self.out_dtype is None else self.out_dtype
 
     @property
     def gh(self) -> int:
@@ -80,7 +85,7 @@ class Geometry:
 
     def c(self) -> nabla_geom:
         return nabla_geom(self.batch, self.heads, self.T, self.H, self.W, self.P, self.head_dim,
-                          _DT.get(self.dtype, -1), self.layout)
+                          _DT.get(self.dtype, -1), self.layout, _DT.get(self.odtype, -1))
 
     def tensor_shape(self, layout: Optional[int] = None) -> Tuple[int, ...]:
         lay = self.layout if layout is None else layout
@@ -90,7 +95,7 @@ class Geometry:
 
     def with_layout(self, layout: int) -> "Geometry":
         return Geometry(self.batch, self.heads, self.T, self.H, self.W, self.head_dim,
-                        self.dtype, layout, self.P)
+                        self.dtype, layout, self.P, self.out_dtype)
 
 
 def _ptr(t: Optional[torch.Tensor], name: str, shape=None, dtype=None) -> Optional[int]:
@@ -192,7 +197,7 @@ def nabla_attn_fwd(g: Geometry, q, k, v, row_ptr, col_idx, scale: float, o, stre
         ctypes.byref(g.c()), _ptr(q, "q", shp, g.dtype), _ptr(k, "k", shp, g.dtype),
         _ptr(v, "v", shp, g.dtype), _ptr(row_ptr, "row_ptr", (bh, g.nb + 1), torch.int32),
         _ptr(col_idx, "col_idx", (bh, g.nb * g.nb), torch.int32), float(scale),
-        _ptr(o, "o", shp, g.dtype), _stream(stream)), "nabla_attn_fwd")
+        _ptr(o, "o", shp, g.odtype), _stream(stream)), "nabla_attn_fwd")
 
 
 def nabla_forward_workspace_size(g: Geometry) -> Tuple[int, Tuple[int, ...]]:
@@ -209,7 +214,7 @@ def nabla_forward(g: Geometry, q, k, v, thr: float, sta, scale: float, o, worksp
     _check(_lib.load().nabla_forward(
         ctypes.byref(g.c()), _ptr(q, "q", shp, g.dtype), _ptr(k, "k", shp, g.dtype),
         _ptr(v, "v", shp, g.dtype), float(thr), _sta(sta), float(scale),
-        _ptr(o, "o", shp, g.dtype), _ptr(workspace, "workspace", None, torch.uint8),
+        _ptr(o, "o", shp, g.odtype), _ptr(workspace, "workspace", None, torch.uint8),
         workspace.numel(), _stream(stream)), "nabla_forward")
 
 
@@ -230,20 +235,22 @@ class ForwardResult:
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, thr: float,
             sta: Optional[Sequence[int]] = (3, 3, 3), scale: Optional[float] = None,
             layout: int = LAYOUT_THW, T: Optional[int] = None, H: Optional[int] = None,
-            W: Optional[int] = None, stream=None) -> ForwardResult:
+            W: Optional[int] = None, out_dtype: Optional[torch.dtype] = None,
+            stream=None) -> ForwardResult:
     """One NABLA attention call.  THW tensors carry T, H, W in their shape;
-    BLOCKED tensors need T, H, W passed explicitly."""
+    BLOCKED tensors need T, H, W passed explicitly.  ``out_dtype`` (default:
+    the input dtype) may be float32 for bf16 inputs."""
     if layout == LAYOUT_THW:
         B, h, T, H, W, d = q.shape
     else:
         B, h, _, _, d = q.shape
         if T is None or H is None or W is None:
             raise ValueError("T, H, W are required for the blocked layout")
-    g = Geometry(B, h, T, H, W, d, q.dtype, layout)
+    g = Geometry(B, h, T, H, W, d, q.dtype, layout, out_dtype=out_dtype)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     size, offs = nabla_forward_workspace_size(g)
     ws = torch.empty(size, dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape, dtype=g.odtype, device=q.device)
     nabla_forward(g, q, k, v, thr, sta, scale, o, ws, stream)
 
     def part(i, dtype, shape):

@@ -28,6 +28,8 @@ int make_geo(const nabla_geom* p, bool layout_used, Geo* g, bool* empty) {
   if (p->P != nabla::kP) return NABLA_E_PATCH;
   if (p->head_dim != 64 && p->head_dim != 128) return NABLA_E_HEAD_DIM;
   if (p->dtype != NABLA_DTYPE_F32 && p->dtype != NABLA_DTYPE_BF16) return NABLA_E_DTYPE;
+  if (p->out_dtype != NABLA_DTYPE_F32 && p->out_dtype != NABLA_DTYPE_BF16) return NABLA_E_DTYPE;
+  if (p->dtype == NABLA_DTYPE_F32 && p->out_dtype != NABLA_DTYPE_F32) return NABLA_E_DTYPE;
   if (layout_used && p->layout != NABLA_LAYOUT_THW && p->layout != NABLA_LAYOUT_BLOCKED)
     return NABLA_E_LAYOUT;
   const int64_t gh = (p->H + 7) / 8, gw = (p->W + 7) / 8;
@@ -104,7 +106,7 @@ const char* nabla_status_string(int status) {
     case NABLA_OK: return "ok";
     case NABLA_E_NULL: return "a required pointer is NULL";
     case NABLA_E_SHAPE: return "invalid shape (batch/heads < 0, T/H/W < 1, or sizes beyond the limits)";
-    case NABLA_E_DTYPE: return "dtype must be NABLA_DTYPE_F32 or NABLA_DTYPE_BF16";
+    case NABLA_E_DTYPE: return "dtype/out_dtype must be F32 or BF16 (F32 inputs need F32 output)";
     case NABLA_E_HEAD_DIM: return "head_dim must be 64 or 128";
     case NABLA_E_PATCH: return "patch side P must be 8";
     case NABLA_E_THR: return "thr must be finite and in (0, 1]";
@@ -205,7 +207,8 @@ int nabla_attn_fwd(const nabla_geom* geom, const void* q, const void* k, const v
   if (q == nullptr || k == nullptr || v == nullptr || row_ptr == nullptr || col_idx == nullptr ||
       o == nullptr)
     return NABLA_E_NULL;
-  return hip_status(nabla::launch_attn_fwd(g, geom->dtype == NABLA_DTYPE_BF16, q, k, v, row_ptr,
+  return hip_status(nabla::launch_attn_fwd(g, geom->dtype == NABLA_DTYPE_BF16,
+                                           geom->out_dtype == NABLA_DTYPE_BF16, q, k, v, row_ptr,
                                            col_idx, scale, o, as_stream(stream)));
 }
 
@@ -252,7 +255,9 @@ int nabla_forward(const nabla_geom* geom, const void* q, const void* k, const vo
   hipError_t e = nabla::launch_pool(g, bf16, q, k, qbar, kbar, s);
   if (e == hipSuccess) e = nabla::launch_mask(g, qbar, kbar, thr, win, bits, cnt, nullptr, s);
   if (e == hipSuccess) e = nabla::launch_compact(g, bits, cnt, rp, ci, s);
-  if (e == hipSuccess) e = nabla::launch_attn_fwd(g, bf16, q, k, v, rp, ci, scale, o, s);
+  if (e == hipSuccess)
+    e = nabla::launch_attn_fwd(g, bf16, geom->out_dtype == NABLA_DTYPE_BF16, q, k, v, rp, ci,
+                               scale, o, s);
   return hip_status(e);
 }
 

@@ -50,12 +50,24 @@ struct AttnShape {
   static constexpr int kDTiles = D / 32;          // 32-row tiles of O^T
 };
 
-template <int D>
+template <typename OutT>
+__device__ inline void store4(OutT* dst, float a, float b, float c, float d);
+template <>
+__device__ inline void store4<__bf16>(__bf16* dst, float a, float b, float c, float d) {
+  bf16x4 v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};   // round to nearest even
+  *(bf16x4*)dst = v;
+}
+template <>
+__device__ inline void store4<float>(float* dst, float a, float b, float c, float d) {
+  *(f32x4*)dst = f32x4{a, b, c, d};
+}
+
+template <int D, typename OutT>
 __global__ void __launch_bounds__(128, 2)
 attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const int32_t* __restrict__ row_ptr,
                      const int32_t* __restrict__ col_idx, float scale_log2,
-                     __bf16* __restrict__ O) {
+                     OutT* __restrict__ O) {
   using A = AttnShape<D>;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[kN * A::kStride];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[kN * A::kStride];
@@ -182,16 +194,22 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
       for (int t = 0; t < A::kDTiles; ++t) oacc[t] *= alpha;
       m_run = m_new;
     }
+    // P^T in bf16; the row sum adds the ROUNDED values (bf16 pairs summed in
+    // fp32 by v_dot2_f32_bf16) so that O / l is an exact convex combination
+    // of V under the weights the matrix cores actually used
     bf16x8 pop[2][2];
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = exp2f(sacc[kt][8 * h + e] - m_run);
-          l_run += p;
-          pop[kt][h][e] = (__bf16)p;
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pr = {(__bf16)exp2f(sacc[kt][8 * h + e] - m_run),
+                             (__bf16)exp2f(sacc[kt][8 * h + e + 1] - m_run)};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+          pop[kt][h][e] = pr[0];
+          pop[kt][h][e + 1] = pr[1];
         }
       }
     }
@@ -217,15 +235,15 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (qvalid || g.layout == 1) {
-    __bf16* orow = O + qoff;
+    OutT* orow = O + qoff;
+    const float sc = qvalid ? inv : 0.f;
 #pragma unroll
     for (int dt = 0; dt < A::kDTiles; ++dt) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(qvalid ? oacc[dt][4 * gq + e] * inv : 0.f);
-        *(bf16x4*)(orow + 32 * dt + 8 * gq + 4 * hl) = v;
+        store4<OutT>(orow + 32 * dt + 8 * gq + 4 * hl, oacc[dt][4 * gq] * sc,
+                     oacc[dt][4 * gq + 1] * sc, oacc[dt][4 * gq + 2] * sc,
+                     oacc[dt][4 * gq + 3] * sc);
       }
     }
   }
@@ -304,33 +322,41 @@ attn_fwd_f32_kernel(const Geo g, const float* __restrict__ Q, const float* __res
   }
 }
 
+template <int D, typename OutT>
+void launch_bf16(const Geo& g, const void* q, const void* k, const void* v,
+                 const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
+                 hipStream_t s) {
+  const float sl2 = scale * 1.4426950408889634f;   // softmax in base 2
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OutT>), dim3((unsigned)(g.bh * g.nb)), dim3(128), 0,
+                     s, g, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
+                     sl2, (OutT*)o);
+}
+
+template <int D>
+void launch_f32(const Geo& g, const void* q, const void* k, const void* v,
+                const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
+                hipStream_t s) {
+  hipLaunchKernelGGL(attn_fwd_f32_kernel<D>, dim3((unsigned)(g.bh * g.nb)), dim3(64), 0, s, g,
+                     (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx, scale,
+                     (float*)o);
+}
+
 }  // namespace
 
-hipError_t launch_attn_fwd(const Geo& g, bool bf16, const void* q, const void* k, const void* v,
-                           const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
-                           hipStream_t s) {
-  const int64_t tiles = g.bh * g.nb;
+hipError_t launch_attn_fwd(const Geo& g, bool bf16, bool out_bf16, const void* q, const void* k,
+                           const void* v, const int32_t* row_ptr, const int32_t* col_idx,
+                           float scale, void* o, hipStream_t s) {
   if (bf16) {
-    const float sl2 = scale * 1.4426950408889634f;   // softmax in base 2
     if (g.d == 64) {
-      hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3((unsigned)tiles), dim3(128), 0, s, g,
-                         (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                         sl2, (__bf16*)o);
+      out_bf16 ? launch_bf16<64, __bf16>(g, q, k, v, row_ptr, col_idx, scale, o, s)
+               : launch_bf16<64, float>(g, q, k, v, row_ptr, col_idx, scale, o, s);
     } else {
-      hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3((unsigned)tiles), dim3(128), 0, s, g,
-                         (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                         sl2, (__bf16*)o);
+      out_bf16 ? launch_bf16<128, __bf16>(g, q, k, v, row_ptr, col_idx, scale, o, s)
+               : launch_bf16<128, float>(g, q, k, v, row_ptr, col_idx, scale, o, s);
     }
   } else {
-    if (g.d == 64) {
-      hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, dim3((unsigned)tiles), dim3(64), 0, s, g,
-                         (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx,
-                         scale, (float*)o);
-    } else {
-      hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, dim3((unsigned)tiles), dim3(64), 0, s, g,
-                         (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx,
-                         scale, (float*)o);
-    }
+    g.d == 64 ? launch_f32<64>(g, q, k, v, row_ptr, col_idx, scale, o, s)
+              : launch_f32<128>(g, q, k, v, row_ptr, col_idx, scale, o, s);
   }
   return hipGetLastError();
 }

@@ -82,8 +82,8 @@ hipError_t launch_mask(const Geo& g, const float* qbar, const float* kbar, float
                        hipStream_t s);
 hipError_t launch_compact(const Geo& g, const uint32_t* bits, const int32_t* cnt,
                           int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
-hipError_t launch_attn_fwd(const Geo& g, bool bf16, const void* q, const void* k, const void* v,
-                           const int32_t* row_ptr, const int32_t* col_idx, float scale,
-                           void* o, hipStream_t s);
+hipError_t launch_attn_fwd(const Geo& g, bool bf16, bool out_bf16, const void* q, const void* k,
+                           const void* v, const int32_t* row_ptr, const int32_t* col_idx,
+                           float scale, void* o, hipStream_t s);
 
 }  // namespace nabla

@@ -45,7 +45,8 @@
  *                         the kernels' address computation)
  *   NABLA_LAYOUT_BLOCKED: tensor [B, heads, nb, 64, d]   (already flattened;
  *                         pad slots present in memory and ignored on input)
- *   Q, K, V and O of one call share one layout and dtype, contiguous.
+ *   Q, K, V and O of one call share one layout, contiguous; Q, K, V share
+ *   `dtype` and O has `out_dtype`.
  *   Pooled tensors qbar, kbar: float32 [B, heads, nb, d].
  *   Masks: uint32 [B, heads, nb, nw], nw = ceil(nb / 32); block c of row r is
  *   kept iff bit (c % 32) of word (c / 32) is set.  Bits >= nb are zero.
@@ -70,7 +71,7 @@ enum nabla_status {
   NABLA_OK = 0,
   NABLA_E_NULL = -1,        /* a required pointer is NULL */
   NABLA_E_SHAPE = -2,       /* batch/heads < 0, T/H/W < 1, or sizes overflow the limits */
-  NABLA_E_DTYPE = -3,       /* dtype not NABLA_DTYPE_F32 / NABLA_DTYPE_BF16 */
+  NABLA_E_DTYPE = -3,       /* dtype / out_dtype not supported (see nabla_geom) */
   NABLA_E_HEAD_DIM = -4,    /* head_dim not 64 or 128 */
   NABLA_E_PATCH = -5,       /* P != 8 */
   NABLA_E_THR = -6,         /* thr not in (0, 1] or not finite */
@@ -95,8 +96,11 @@ typedef struct nabla_geom {
   int32_t T, H, W;   /* valid latent extents, each >= 1 */
   int32_t P;         /* patch side; must be 8 */
   int32_t head_dim;  /* d: 64 or 128 */
-  int32_t dtype;     /* enum nabla_dtype: element type of Q, K, V, O */
+  int32_t dtype;     /* enum nabla_dtype: element type of Q, K, V */
   int32_t layout;    /* enum nabla_layout: layout of Q, K, V, O */
+  int32_t out_dtype; /* enum nabla_dtype: element type of O; float32 inputs
+                        need float32 output, bf16 inputs may write either (the
+                        bf16 output is the float32 result rounded once, RNE) */
 } nabla_geom;
 
 /* Number of blocks per head, nb (see Geometry above). */
@@ -153,7 +157,8 @@ int nabla_compact(const nabla_geom* geom, const uint32_t* mask_bits,
  * i of block r, o_i = sum_j softmax_j(q_i . k_j * scale) v_j over the valid
  * key tokens j of the kept blocks listed for row r.  bf16 inputs use bf16
  * matrix cores with float32 accumulation and a float32 online softmax;
- * float32 inputs compute in float32.  q, k, v, o in geom's layout and dtype;
+ * float32 inputs compute in float32.  q, k, v in geom's layout and dtype, o
+ * in geom's layout and out_dtype;
  * in NABLA_LAYOUT_BLOCKED pad query slots of o are written as zeros.  A row
  * with an empty list produces zeros.  scale > 0 (usually 1/sqrt(d)).
  * col_idx entries must lie in [0, nb). */

@@ -24,9 +24,9 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
-def geom_of(cfg: synth.Config, layout=nabla.LAYOUT_THW) -> nabla.Geometry:
+def geom_of(cfg: synth.Config, layout=nabla.LAYOUT_THW, out_dtype=None) -> nabla.Geometry:
     return nabla.Geometry(cfg.batch, cfg.heads, cfg.T, cfg.H, cfg.W, cfg.head_dim,
-                          cfg.torch_dtype, layout)
+                          cfg.torch_dtype, layout, out_dtype=out_dtype)
 
 
 def ogeom(cfg: synth.Config) -> O.Geometry:
@@ -48,10 +48,13 @@ def tol(dtype: torch.dtype):
     return (BF16_MAX_ABS, BF16_MEAN_ABS) if dtype == torch.bfloat16 else (F32_MAX_ABS, F32_MEAN_ABS)
 
 
-def run_pipeline(cfg: synth.Config, q, k, v, layout=nabla.LAYOUT_THW, thr=None, sta=None):
+def run_pipeline(cfg: synth.Config, q, k, v, layout=nabla.LAYOUT_THW, thr=None, sta=None,
+                 out_dtype=torch.float32, also_bf16=False):
     """Run pool -> mask -> compact -> attn through the C ABI, one entry point
-    at a time (the launch sequence bench.py times)."""
-    g = geom_of(cfg, layout)
+    at a time (the launch sequence bench.py times).  The output is float32 by
+    default (the kernel's result before any rounding to bf16); with
+    ``also_bf16`` the attention is run a second time writing bf16 (o_bf16)."""
+    g = geom_of(cfg, layout, out_dtype)
     thr = cfg.thr if thr is None else thr
     sta = cfg.sta if sta is None else sta
     dev = q.device
@@ -63,13 +66,27 @@ def run_pipeline(cfg: synth.Config, q, k, v, layout=nabla.LAYOUT_THW, thr=None, 
     cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)
     rp = torch.empty((B * h, nb + 1), dtype=torch.int32, device=dev)
     ci = torch.empty((B * h, nb * nb), dtype=torch.int32, device=dev)
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape, dtype=g.odtype, device=dev)
     nabla.nabla_pool(g, q, k, qbar, kbar)
     nabla.nabla_mask(g, qbar, kbar, thr, sta, bits, cnt, abits)
     nabla.nabla_compact(g, bits, cnt, rp, ci)
     nabla.nabla_attn_fwd(g, q, k, v, rp, ci, 1.0 / math.sqrt(d), o)
+    out = dict(g=g, qbar=qbar, kbar=kbar, bits=bits, abits=abits, cnt=cnt, rp=rp, ci=ci, o=o)
+    if also_bf16 and q.dtype == torch.bfloat16:
+        gb = geom_of(cfg, layout, torch.bfloat16)
+        ob = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        nabla.nabla_attn_fwd(gb, q, k, v, rp, ci, 1.0 / math.sqrt(d), ob)
+        out["o_bf16"] = ob
     torch.cuda.synchronize()
-    return dict(g=g, qbar=qbar, kbar=kbar, bits=bits, abits=abits, cnt=cnt, rp=rp, ci=ci, o=o)
+    return out
+
+
+def check_bf16_rounding(res) -> None:
+    """The bf16 output is the float32 result rounded once to nearest even."""
+    if "o_bf16" in res:
+        want = res["o"].to(torch.bfloat16)
+        assert torch.equal(res["o_bf16"].view(torch.int16), want.view(torch.int16)), \
+            "bf16 output is not the float32 result rounded to nearest even"
 
 
 def oracle_mask(cfg: synth.Config, q_h: np.ndarray, k_h: np.ndarray, thr=None, sta=None):

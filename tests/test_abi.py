@@ -40,7 +40,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def G(**kw):
-    base = dict(batch=1, heads=2, T=4, H=16, W=16, P=8, head_dim=64, dtype=1, layout=0)
+    base = dict(batch=1, heads=2, T=4, H=16, W=16, P=8, head_dim=64, dtype=1, layout=0,
+                out_dtype=1)
     base.update(kw)
     return _lib.nabla_geom(*[base[f] for f, _ in _lib.nabla_geom._fields_])
 
@@ -51,6 +52,7 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case below fails va
 @pytest.mark.parametrize("geom,status", [
     (dict(batch=-1), -2), (dict(heads=-3), -2), (dict(T=0), -2), (dict(H=0), -2), (dict(W=-1), -2),
     (dict(P=4), -5), (dict(head_dim=96), -4), (dict(dtype=7), -3), (dict(layout=5), -9),
+    (dict(out_dtype=2), -3), (dict(dtype=0, out_dtype=1), -3),
     (dict(T=100, H=64, W=64), -12), (dict(batch=300, heads=300), -2),
 ])
 def test_geometry_validation(geom, status):

@@ -8,8 +8,8 @@ import torch
 
 import oracle as O
 import synth
-from gpu_helpers import (check_mask_rows, check_output, f64, log, ogeom, oracle_mask,
-                         run_pipeline, unpack_bits)
+from gpu_helpers import (check_bf16_rounding, check_mask_rows, check_output, f64, log, ogeom,
+                         oracle_mask, run_pipeline, unpack_bits)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -27,7 +27,8 @@ def _sample_rows(cfg, nb):
 def _run(cfg, q, k, v, thr=None, sta=None, label=""):
     thr = cfg.thr if thr is None else thr
     sta = cfg.sta if sta is None else sta
-    res = run_pipeline(cfg, q, k, v, thr=thr, sta=sta)
+    res = run_pipeline(cfg, q, k, v, thr=thr, sta=sta, also_bf16=True)
+    check_bf16_rounding(res)
     nb = res["g"].nb
     og = ogeom(cfg)
     heads = synth.sampled_heads(cfg)

@@ -9,8 +9,8 @@ import torch
 import block_sparse_attention_flatten_amd as nabla
 import oracle as O
 import synth
-from gpu_helpers import (check_mask_rows, check_output, f64, geom_of, log, ogeom,
-                         oracle_mask, run_pipeline, unpack_bits)
+from gpu_helpers import (check_bf16_rounding, check_mask_rows, check_output, f64, geom_of,
+                         log, ogeom, oracle_mask, run_pipeline, unpack_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -88,7 +88,8 @@ def test_pool(case, layout):
 def test_mask_and_forward(case):
     """pool -> mask -> compact -> attention through the C ABI vs the oracle."""
     name, cfg, q, k, v = case
-    res = run_pipeline(cfg, q, k, v)
+    res = run_pipeline(cfg, q, k, v, also_bf16=True)
+    check_bf16_rounding(res)
     g = res["g"]
     nb = g.nb
     union = unpack_bits(res["bits"], nb)
@@ -130,7 +131,7 @@ def test_attention_with_oracle_masks(case):
     """Attention kernel alone, fed the oracle's mask (and random masks with
     one-block, empty-ish and full rows) as CSR."""
     name, cfg, q, k, v = case
-    g = geom_of(cfg)
+    g = geom_of(cfg, out_dtype=torch.float32)
     og = ogeom(cfg)
     nb = g.nb
     rng = np.random.default_rng(11)
@@ -153,7 +154,7 @@ def test_attention_with_oracle_masks(case):
             p_, c_ = O.to_csr(masks[b][h])
             rp[b * cfg.heads + h] = p_
             ci[b * cfg.heads + h, :len(c_)] = c_
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     nabla.nabla_attn_fwd(g, q, k, v, torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda(),
                          1.0 / math.sqrt(cfg.head_dim), o)
     torch.cuda.synchronize()
@@ -197,10 +198,13 @@ def test_forward_entry_point_matches_stepwise():
     """nabla_forward (one call) == the four entry points called one by one, bit for bit."""
     cfg = synth.config("small", heads=3, T=3, H=21, W=30, thr=0.75, sta=(3, 3, 3))
     q, k, v = synth.make_qkv(cfg, device="cuda")
-    step = run_pipeline(cfg, q, k, v)
+    step = run_pipeline(cfg, q, k, v, out_dtype=torch.bfloat16)
     res = nabla.forward(q, k, v, cfg.thr, cfg.sta)
     torch.cuda.synchronize()
     assert torch.equal(res.o.view(torch.int16), step["o"].view(torch.int16))
+    res32 = nabla.forward(q, k, v, cfg.thr, cfg.sta, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(res32.o.to(torch.bfloat16).view(torch.int16), res.o.view(torch.int16))
     assert torch.equal(res.mask_bits, step["bits"])
     assert torch.equal(res.row_ptr, step["rp"])
 
