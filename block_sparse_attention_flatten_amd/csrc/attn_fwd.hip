@@ -42,7 +42,12 @@ __device__ inline int64_t xcd_tile(int64_t bid, int64_t n) {
 
 template <int D>
 struct AttnShape {
-  static constexpr int kStride = D + 8;           // LDS row stride (elements): 16 B pad
+  // LDS row strides (elements).  K rows are read as 16-byte operand rows by 32
+  // lanes: a stride of 4 (mod 32) banks spreads 8 consecutive rows over all
+  // banks.  V rows are read by transpose loads, 4 rows x 32 bytes per 16-lane
+  // group: a stride of 8 (mod 32) banks keeps those 4 rows disjoint.
+  static constexpr int kStride = D + 8;
+  static constexpr int kVStride = D + 16;
   static constexpr int kChunks = D / 8;           // 16-byte chunks per token row
   static constexpr int kRowsPerPass = 128 / kChunks;
   static constexpr int kPasses = kN / kRowsPerPass;
@@ -70,7 +75,7 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
                      OutT* __restrict__ O) {
   using A = AttnShape<D>;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[kN * A::kStride];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[kN * A::kStride];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[kN * A::kVStride];
 
   const int nb = g.nb;
   const int64_t tile = xcd_tile(blockIdx.x, (int64_t)gridDim.x);
@@ -149,7 +154,7 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
     for (int p = 0; p < A::kPasses; ++p) {
       const int r = ld_row + p * A::kRowsPerPass;
       *(u32x4*)(Ks + r * A::kStride + ld_chunk * 8) = kreg[p];
-      *(u32x4*)(Vs + r * A::kStride + ld_chunk * 8) = vreg[p];
+      *(u32x4*)(Vs + r * A::kVStride + ld_chunk * 8) = vreg[p];
     }
     __syncthreads();
     if (idx + 1 < end) fetch(col_at(idx + 1));
@@ -168,22 +173,23 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
     const BlockCoord bc = block_coord(g, beta < 0 ? 0 : beta);
     const int rv = beta < 0 ? 0 : block_rows_valid(g, bc);
     const int cv = block_cols_valid(g, bc);
-    const bool edge = rv < kP || cv < kP;
+    if (rv < kP || cv < kP) {        // latent-edge block: pad keys get -inf
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (!((key >> 3) < rv && (key & 7) < cv)) sacc[kt][r] = -INFINITY;
+        }
+      }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sacc[kt][r] * scale_log2;
-        if (edge) {
-          const int key = 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (!((key >> 3) < rv && (key & 7) < cv)) x = -INFINITY;
-        }
-        sacc[kt][r] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
     // move the reference only when needed (wavefront-uniform decision)
     const bool grow = mx > m_run + 8.0f;
     if (__any(grow)) {
@@ -205,8 +211,9 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const bf16x2 pr = {(__bf16)exp2f(sacc[kt][8 * h + e] - m_run),
-                             (__bf16)exp2f(sacc[kt][8 * h + e + 1] - m_run)};
+          const bf16x2 pr = {
+              (__bf16)exp2f(__builtin_fmaf(sacc[kt][8 * h + e], scale_log2, -m_run)),
+              (__bf16)exp2f(__builtin_fmaf(sacc[kt][8 * h + e + 1], scale_log2, -m_run))};
           l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
           pop[kt][h][e] = pr[0];
           pop[kt][h][e + 1] = pr[1];
@@ -214,17 +221,25 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
       }
     }
     // ---- O^T (d x 32 queries) += V^T P^T ----
+    // A operand (V^T rows d = 32dt + lane%32, keys k0..k0+3, k0+8..k0+11 with
+    // k0 = 32kt + 16h + 4hl) straight from the row-major V tile with two
+    // transpose loads: in each 16-lane group, lane i receives element i%4 of
+    // the 4-element rows addressed by lanes 4e + i/4 (e = 0..3), so lane s of
+    // the group addresses key k0 + s/4 (+8), columns d0 + 4(s%4) .. +3.
+    const __bf16* vsrc = Vs + ((lane & 15) >> 2) * A::kVStride + (lane & 16) + 4 * (lane & 3);
 #pragma unroll
     for (int dt = 0; dt < A::kDTiles; ++dt) {
-      const __bf16* vcol = Vs + 32 * dt + jl;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int k0 = 32 * kt + 16 * h + 4 * hl;   // keys k0..k0+3 and k0+8..k0+11
-          bf16x8 a;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) a[e] = vcol[(k0 + (e < 4 ? e : e + 4)) * A::kStride];
+          const int k0 = 32 * kt + 16 * h + 4 * hl;
+          const __bf16* src = vsrc + k0 * A::kVStride + 32 * dt;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(src));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(src + 8 * A::kVStride));
+          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[kt][h], oacc[dt], 0, 0, 0);
         }
       }
