@@ -47,10 +47,27 @@ def parse():
     ap.add_argument("--config", default="720p", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--thr", type=float, default=None)
     ap.add_argument("--sta", type=str, default=None, help="e.g. 3,3,3 or 0,0,0")
+    ap.add_argument("--heads", type=int, default=None, help="override the head count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 2 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE
+    counter readings calibrate the counters of the NABLA kernels."""
+    import torch
+    n = 1 << 29                                   # 2 GiB of float32
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
 
 
 def algorithmic_bytes(cfg, nb, nnz_total):
@@ -116,6 +133,9 @@ def cpu_baseline(cfg, q, k, v, thr, sta, budget_s):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the NABLA call "
               "shards by head with no communication, so run it per GPU.", file=sys.stderr)
@@ -127,6 +147,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = synth.config(args.config)
+    if args.heads is not None:
+        cfg = cfg.with_(heads=args.heads)
     thr = cfg.thr if args.thr is None else args.thr
     sta = cfg.sta if args.sta is None else tuple(int(x) for x in args.sta.split(","))
     log(f"config {cfg.name}: {cfg} thr={thr} sta={sta}")
@@ -231,7 +253,8 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic (seeded smooth spatio-temporal fields + noise; no weights)",
         "config": {
-            "workload": WORKLOAD_NAMES[cfg.name],
+            "workload": WORKLOAD_NAMES[cfg.name] + (
+                f" [heads overridden to {cfg.heads}]" if args.heads is not None else ""),
             "batch": B, "heads": h, "head_dim": d, "latent_THW": [cfg.T, cfg.H, cfg.W],
             "patch": cfg.P, "blocks_per_head": nb, "tokens_padded": nb * 64,
             "thr": thr, "sta": list(sta),

@@ -4,40 +4,72 @@
 // lsdiaocha.cn article, sec. 2 step 3: each kept reduced entry stands for a
 // whole N x N block computed exactly).
 //
-// bf16 path, gfx950 matrix cores.  One workgroup of two wavefronts computes one
-// query block (64 tokens) of one head; wavefront w owns queries 32w..32w+31.
-// For every kept key block listed in the CSR row:
-//   * the K and V tiles (64 x d bf16 each) are staged in LDS; the next tile is
-//     prefetched into registers while the current one is computed;
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so that the 32 scores a lane
-//     holds all belong to ONE query (its column) -- the online softmax needs
-//     one cross-lane exchange (lane l <-> l^32) per block for the row max and
-//     none for the row sum (each lane keeps a partial sum);
+// bf16 path, gfx950 matrix cores.  The kernel is bound by how often a K/V tile
+// must come from beyond the XCD's L2, so one workgroup serves TWO query blocks
+// that see similar keys -- the same 8x8 patch in two consecutive frames (an
+// odd last frame pairs horizontal neighbours) -- and walks the merged,
+// ascending union of their kept lists: every K/V tile in the union is fetched
+// once for both.  Four wavefronts: 0-1 own the first query block, 2-3 the
+// second, 32 queries each.  For every block of the union:
+//   * all 256 threads load the K and V tiles (64 x d bf16 each) into LDS; the
+//     next tile of the union is prefetched into registers meanwhile;
+//   * a wavefront whose query block does not keep this key block skips it;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so the 32 scores a lane
+//     holds belong to ONE query: the online softmax needs one cross-lane
+//     exchange (lane l <-> l^32) per block for the row max and none for the
+//     row sum (each lane keeps a partial sum);
 //   * P^T is converted to bf16 in registers and used directly as the B
-//     operand of O^T += V^T P^T; the contraction over the 64 keys follows the
-//     order in which the lane holds P^T, and the matching V^T elements are
-//     gathered from the row-major V tile in LDS;
-//   * the running max is only moved when a block's max exceeds it by more
-//     than 2^8 in the exp2 domain (exact: O and the row sum always share the
-//     same reference), which skips most rescales of the 64 O registers.
+//     operand of O^T += V^T P^T; the V^T operand comes from the row-major V
+//     tile through ds_read_b64_tr_b16 transpose loads;
+//   * the running max only moves when a block's max exceeds it by more than
+//     2^8 in the exp2 domain (exact: O and the row sum share the reference).
 // Pad keys (latent edge blocks) get -inf scores; pad queries are not written
-// (blocked layout: written as zeros).  Workgroups are remapped so that each
-// XCD walks a contiguous range of (head, query block) tiles, which keeps
-// neighbouring query blocks' K/V in that XCD's L2.
+// (blocked layout: written as zeros).
 //
 // fp32 path: a plain kernel (one thread per query, fp32 FMA, K/V tiles in
 // LDS) used for float32 inputs.
+#include <limits.h>
+
 #include "nabla_common.hpp"
 
 namespace nabla {
 
 namespace {
 
-// Workgroup id -> tile id such that XCD x (= bid % 8) gets a contiguous range.
-__device__ inline int64_t xcd_tile(int64_t bid, int64_t n) {
-  const int64_t q = n >> 3, r = n & 7;
-  const int64_t x = bid & 7, i = bid >> 3;
-  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+// Pair work items of one head: item p -> query blocks (a, b), b = -1 when a
+// has no partner.  Pairs are (t, hb, wb) and (t + 1, hb, wb) for even t; when
+// T is odd the last frame pairs (hb, wb) with (hb, wb + 1) for even wb.
+__host__ __device__ inline int pair_items(const Geo& g) {
+  const int pf = g.gh * g.gw;
+  return (g.T >> 1) * pf + ((g.T & 1) ? g.gh * ((g.gw + 1) >> 1) : 0);
+}
+__device__ inline void pair_of(const Geo& g, int p, int* a, int* b) {
+  const int pf = g.gh * g.gw;
+  const int nfull = (g.T >> 1) * pf;
+  if (p < nfull) {
+    const int t2 = p / pf;
+    *a = 2 * t2 * pf + (p - t2 * pf);
+    *b = *a + pf;
+    return;
+  }
+  const int q = p - nfull, hw = (g.gw + 1) >> 1;
+  const int hb = q / hw, wp = q - hb * hw;
+  *a = (g.T - 1) * pf + hb * g.gw + 2 * wp;
+  *b = 2 * wp + 1 < g.gw ? *a + 1 : -1;
+}
+
+// Workgroup id -> (head, pair item).  Workgroups are dispatched in id order,
+// round-robin over the 8 XCDs (XCD = id % 8).  Each head's items are cut into
+// 8 contiguous chunks and XCD x takes chunk x of every head in turn: all XCDs
+// work on the same head at any time and each XCD's L2 sees one compact
+// spatial region whose kept lists overlap.  False for padding ids.
+__device__ inline bool xcd_item(int bid, int items, int chunk, int64_t* head, int* item) {
+  const int x = bid & 7, i = bid >> 3;
+  const int h = i / chunk;
+  const int it = x * chunk + (i - h * chunk);
+  *head = h;
+  *item = it;
+  return it < items;
 }
 
 template <int D>
@@ -48,8 +80,9 @@ struct AttnShape {
   // group: a stride of 8 (mod 32) banks keeps those 4 rows disjoint.
   static constexpr int kStride = D + 8;
   static constexpr int kVStride = D + 16;
+  static constexpr int kThreads = 256;
   static constexpr int kChunks = D / 8;           // 16-byte chunks per token row
-  static constexpr int kRowsPerPass = 128 / kChunks;
+  static constexpr int kRowsPerPass = kThreads / kChunks;
   static constexpr int kPasses = kN / kRowsPerPass;
   static constexpr int kSteps = D / 16;           // k-steps of S^T = K Q^T
   static constexpr int kDTiles = D / 32;          // 32-row tiles of O^T
@@ -67,8 +100,31 @@ __device__ inline void store4<float>(float* dst, float a, float b, float c, floa
   *(f32x4*)dst = f32x4{a, b, c, d};
 }
 
+// Ascending kept list of one query block, read through the scalar cache;
+// entries outside [0, nb) are skipped so a malformed list cannot cause wild
+// reads.
+struct KeptList {
+  const int32_t* p;
+  int i, n, nb;
+  __device__ int peek() {
+    while (i < n && (unsigned)p[i] >= (unsigned)nb) ++i;
+    return i < n ? p[i] : INT_MAX;
+  }
+};
+
+__device__ inline KeptList kept_list(const int32_t* row_ptr, const int32_t* cols, int nb, int q) {
+  KeptList l = {cols, 0, 0, nb};
+  if (q < 0) return l;
+  const int begin = row_ptr[q];
+  const int end = row_ptr[q + 1];
+  if (begin < 0 || end < begin || end > nb * nb) return l;   // malformed row: no keys
+  l.p = cols + begin;
+  l.n = end - begin;
+  return l;
+}
+
 template <int D, typename OutT>
-__global__ void __launch_bounds__(128, 2)
+__global__ void __launch_bounds__(256, 2)
 attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const int32_t* __restrict__ row_ptr,
                      const int32_t* __restrict__ col_idx, float scale_log2,
@@ -78,22 +134,32 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
   __shared__ __attribute__((aligned(16))) __bf16 Vs[kN * A::kVStride];
 
   const int nb = g.nb;
-  const int64_t tile = xcd_tile(blockIdx.x, (int64_t)gridDim.x);
-  const int64_t head = tile / nb;
-  const int qb = (int)(tile - head * nb);
+  const int items = pair_items(g);
+  int64_t head;
+  int item;
+  if (!xcd_item(blockIdx.x, items, (items + 7) >> 3, &head, &item)) return;
+  int qa, qpair;
+  pair_of(g, item, &qa, &qpair);
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int grp = wave >> 1;         // 0: first query block of the pair, 1: second
   const int hl = lane >> 5;          // lane half
   const int jl = lane & 31;          // query column / operand row of this lane
+  const int myq = grp == 0 ? qa : qpair;   // -1: this wavefront only helps load
   const int64_t hoff = head * (int64_t)g.head_elems;
   const int row_step = block_row_step(g);
 
   // ---- this lane's query row as the B operand of S^T = K Q^T ----
-  const int qs = 32 * wave + jl;     // slot in the query block
-  const BlockCoord qc = block_coord(g, qb);
-  const bool qvalid = (qs >> 3) < block_rows_valid(g, qc) && (qs & 7) < block_cols_valid(g, qc);
-  const int64_t qoff = hoff + block_base(g, qb, qc) + (qs >> 3) * row_step + (qs & 7) * D;
+  const int qs = 32 * (wave & 1) + jl;   // slot in the query block
+  bool qvalid = false;
+  int64_t qoff = 0;
+  if (myq >= 0) {
+    const BlockCoord qc = block_coord(g, myq);
+    qvalid = (qs >> 3) < block_rows_valid(g, qc) && (qs & 7) < block_cols_valid(g, qc);
+    qoff = hoff + block_base(g, myq, qc) + (qs >> 3) * row_step + (qs & 7) * D;
+  }
   bf16x8 qop[A::kSteps];
 #pragma unroll
   for (int s = 0; s < A::kSteps; ++s) {
@@ -111,44 +177,42 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
   float l_run = 0.f;                 // partial row sum over the keys this lane holds
 
   const int32_t* rp = row_ptr + head * (nb + 1);
-  const int begin = rp[qb];
-  int end = rp[qb + 1];
-  if (begin < 0 || end < begin || end > nb * nb) end = begin;   // malformed row: no keys
   const int32_t* cols = col_idx + head * (int64_t)nb * nb;
+  KeptList la = kept_list(rp, cols, nb, qa);
+  KeptList lb = kept_list(rp, cols, nb, qpair);
 
   // loader mapping: thread -> (chunk, first row); rows advance by kRowsPerPass
   const int ld_chunk = tid % A::kChunks;
   const int ld_row = tid / A::kChunks;
   u32x4 kreg[A::kPasses], vreg[A::kPasses];
 
+  // Pad key rows (latent edge) load row 0 of the same block instead: any
+  // finite data will do, since their scores are set to -inf and their P to 0.
   auto fetch = [&](int beta) {
-    const BlockCoord bc = block_coord(g, beta < 0 ? 0 : beta);
-    const int rv = beta < 0 ? 0 : block_rows_valid(g, bc);
+    const BlockCoord bc = block_coord(g, beta);
+    const int rv = block_rows_valid(g, bc);
     const int cv = block_cols_valid(g, bc);
-    const int64_t base = hoff + block_base(g, beta, bc);
+    const __bf16* kb = K + hoff + block_base(g, beta, bc) + ld_chunk * 8;
+    const __bf16* vb = V + hoff + block_base(g, beta, bc) + ld_chunk * 8;
 #pragma unroll
     for (int p = 0; p < A::kPasses; ++p) {
       const int r = ld_row + p * A::kRowsPerPass;
-      if ((r >> 3) < rv && (r & 7) < cv) {
-        const int64_t off = base + (r >> 3) * row_step + (r & 7) * D + ld_chunk * 8;
-        kreg[p] = *(const u32x4*)(K + off);
-        vreg[p] = *(const u32x4*)(V + off);
-      } else {
-        kreg[p] = u32x4{0u, 0u, 0u, 0u};
-        vreg[p] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const bool ok = (r >> 3) < rv && (r & 7) < cv;
+      const int off = ok ? (r >> 3) * row_step + (r & 7) * D : 0;
+      kreg[p] = *(const u32x4*)(kb + off);
+      vreg[p] = *(const u32x4*)(vb + off);
     }
   };
 
-  // block indices outside [0, nb) are replaced by an all-pad block (never
-  // loaded, all keys masked): a malformed list cannot cause wild reads
-  auto col_at = [&](int idx) {
-    const int c = cols[idx];
-    return (unsigned)c < (unsigned)nb ? c : -1;
-  };
-  if (begin < end) fetch(col_at(begin));
-  for (int idx = begin; idx < end; ++idx) {
-    const int beta = col_at(idx);
+  int next = min(la.peek(), lb.peek());      // next key block of the merged union
+  if (next != INT_MAX) fetch(next);
+  while (next != INT_MAX) {
+    const int beta = next;
+    const bool in_a = la.peek() == beta;
+    const bool in_b = lb.peek() == beta;
+    la.i += in_a;
+    lb.i += in_b;
+    next = min(la.peek(), lb.peek());
     __syncthreads();                 // every wavefront is done with the previous tile
 #pragma unroll
     for (int p = 0; p < A::kPasses; ++p) {
@@ -157,7 +221,8 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
       *(u32x4*)(Vs + r * A::kVStride + ld_chunk * 8) = vreg[p];
     }
     __syncthreads();
-    if (idx + 1 < end) fetch(col_at(idx + 1));
+    if (next != INT_MAX) fetch(next);
+    if (!(grp == 0 ? in_a : in_b)) continue;   // wavefront-uniform: not a kept block of ours
 
     // ---- S^T (64 keys x 32 queries) ----
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
@@ -170,8 +235,8 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
       }
     }
     // element r of sacc[kt] is key 32kt + 8(r/4) + 4hl + (r%4) of this lane's query
-    const BlockCoord bc = block_coord(g, beta < 0 ? 0 : beta);
-    const int rv = beta < 0 ? 0 : block_rows_valid(g, bc);
+    const BlockCoord bc = block_coord(g, beta);
+    const int rv = block_rows_valid(g, bc);
     const int cv = block_cols_valid(g, bc);
     if (rv < kP || cv < kP) {        // latent-edge block: pad keys get -inf
 #pragma unroll
@@ -200,9 +265,11 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
       for (int t = 0; t < A::kDTiles; ++t) oacc[t] *= alpha;
       m_run = m_new;
     }
-    // P^T in bf16; the row sum adds the ROUNDED values (bf16 pairs summed in
-    // fp32 by v_dot2_f32_bf16) so that O / l is an exact convex combination
-    // of V under the weights the matrix cores actually used
+    // P^T in bf16 (v_exp_f32 directly: its inputs are <= 8, and results below
+    // the fp32 normal range flush to 0, which only drops weights < 2^-126);
+    // the row sum adds the ROUNDED values (bf16 pairs summed in fp32 by
+    // v_dot2_f32_bf16) so that O / l is an exact convex combination of V
+    // under the weights the matrix cores actually used
     bf16x8 pop[2][2];
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
@@ -211,9 +278,10 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const bf16x2 pr = {
-              (__bf16)exp2f(__builtin_fmaf(sacc[kt][8 * h + e], scale_log2, -m_run)),
-              (__bf16)exp2f(__builtin_fmaf(sacc[kt][8 * h + e + 1], scale_log2, -m_run))};
+          const float x0 = __builtin_fmaf(sacc[kt][8 * h + e], scale_log2, -m_run);
+          const float x1 = __builtin_fmaf(sacc[kt][8 * h + e + 1], scale_log2, -m_run);
+          const bf16x2 pr = {(__bf16)__builtin_amdgcn_exp2f(x0),
+                             (__bf16)__builtin_amdgcn_exp2f(x1)};
           l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
           pop[kt][h][e] = pr[0];
           pop[kt][h][e + 1] = pr[1];
@@ -249,7 +317,7 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
   // ---- normalise and write this lane's query row ----
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (qvalid || g.layout == 1) {
+  if (myq >= 0 && (qvalid || g.layout == 1)) {
     OutT* orow = O + qoff;
     const float sc = qvalid ? inv : 0.f;
 #pragma unroll
@@ -342,8 +410,9 @@ void launch_bf16(const Geo& g, const void* q, const void* k, const void* v,
                  const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
                  hipStream_t s) {
   const float sl2 = scale * 1.4426950408889634f;   // softmax in base 2
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OutT>), dim3((unsigned)(g.bh * g.nb)), dim3(128), 0,
-                     s, g, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
+  const int64_t chunk = (pair_items(g) + 7) / 8;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OutT>), dim3((unsigned)(8 * chunk * g.bh)),
+                     dim3(AttnShape<D>::kThreads), 0, s, g, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
                      sl2, (OutT*)o);
 }
 
