@@ -52,6 +52,8 @@ int make_geo(const nabla_geom* p, bool layout_used, Geo* g, bool* empty) {
   g->d = p->head_dim;
   g->layout = p->layout == NABLA_LAYOUT_BLOCKED ? 1 : 0;
   g->head_elems = (int)(g->layout == 1 ? blk : thw);
+  g->per_frame_r = nabla::make_recip((uint32_t)(gh * gw));
+  g->gw_r = nabla::make_recip((uint32_t)gw);
   *empty = bh == 0;
   return NABLA_OK;
 }

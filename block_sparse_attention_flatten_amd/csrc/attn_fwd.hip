@@ -100,26 +100,29 @@ __device__ inline void store4<float>(float* dst, float a, float b, float c, floa
   *(f32x4*)dst = f32x4{a, b, c, d};
 }
 
-// Ascending kept list of one query block, read through the scalar cache;
-// entries outside [0, nb) are skipped so a malformed list cannot cause wild
-// reads.
+// Ascending kept list of one query block, read through the scalar cache (the
+// constant address space makes these uniform reads scalar loads); entries
+// outside [0, nb) are skipped so a malformed list cannot cause wild reads.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
 struct KeptList {
-  const int32_t* p;
+  const_i32* p;
   int i, n, nb;
-  __device__ int peek() {
+  int head;                          // p[i] (first valid entry from i on), INT_MAX at the end
+  __device__ void settle() {
     while (i < n && (unsigned)p[i] >= (unsigned)nb) ++i;
-    return i < n ? p[i] : INT_MAX;
+    head = i < n ? p[i] : INT_MAX;
   }
 };
 
 __device__ inline KeptList kept_list(const int32_t* row_ptr, const int32_t* cols, int nb, int q) {
-  KeptList l = {cols, 0, 0, nb};
+  KeptList l = {(const_i32*)cols, 0, 0, nb, INT_MAX};
   if (q < 0) return l;
-  const int begin = row_ptr[q];
-  const int end = row_ptr[q + 1];
+  const int begin = ((const_i32*)row_ptr)[q];
+  const int end = ((const_i32*)row_ptr)[q + 1];
   if (begin < 0 || end < begin || end > nb * nb) return l;   // malformed row: no keys
-  l.p = cols + begin;
+  l.p = (const_i32*)(cols + begin);
   l.n = end - begin;
+  l.settle();
   return l;
 }
 
@@ -204,15 +207,15 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
     }
   };
 
-  int next = min(la.peek(), lb.peek());      // next key block of the merged union
+  int next = min(la.head, lb.head);          // next key block of the merged union
   if (next != INT_MAX) fetch(next);
   while (next != INT_MAX) {
     const int beta = next;
-    const bool in_a = la.peek() == beta;
-    const bool in_b = lb.peek() == beta;
-    la.i += in_a;
-    lb.i += in_b;
-    next = min(la.peek(), lb.peek());
+    const bool in_a = la.head == beta;
+    const bool in_b = lb.head == beta;
+    if (in_a) { ++la.i; la.settle(); }
+    if (in_b) { ++lb.i; lb.settle(); }
+    next = min(la.head, lb.head);
     __syncthreads();                 // every wavefront is done with the previous tile
 #pragma unroll
     for (int p = 0; p < A::kPasses; ++p) {

@@ -22,14 +22,31 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 // Geometry of one call.  Blocks are P x P spatial patches of one frame
 // ("NABLA: Neighborhood Adaptive Block-Level Attention", gist.science,
 // Methodology: token reordering); H and W are padded up to Hp, Wp.
+// Division of n < 2^16 by a fixed d <= 2^16 without a divide sequence:
+// with m = floor(2^32 / d) + 1 split as (hi, lo) at 2^32,
+// n / d == hi * n + ((n * lo) >> 32) exactly (error of n*m/2^32 is < 2^-16 <= 1/d).
+struct Recip {
+  uint32_t lo;
+  uint32_t hi;
+};
+inline Recip make_recip(uint32_t d) {
+  const uint64_t m = (((uint64_t)1) << 32) / d + 1;
+  return Recip{(uint32_t)m, (uint32_t)(m >> 32)};
+}
+__host__ __device__ inline int div16(int n, Recip r) {
+  return (int)(r.hi * (uint32_t)n + (uint32_t)(((uint64_t)(uint32_t)n * r.lo) >> 32));
+}
+
 struct Geo {
   int64_t bh;        // batch * heads
   int T, H, W;       // valid extents
   int gh, gw;        // block rows / columns per frame (Hp / 8, Wp / 8)
-  int nb;            // blocks per head
+  int nb;            // blocks per head (< 2^16)
   int d;             // head dim
   int layout;        // 0: [.., T, H, W, d]   1: [.., nb, 64, d]
   int head_elems;    // elements per head in the tensor layout (< 2^31)
+  Recip per_frame_r; // division by gh * gw
+  Recip gw_r;        // division by gw
 };
 
 struct BlockCoord {
@@ -37,11 +54,10 @@ struct BlockCoord {
 };
 
 __host__ __device__ inline BlockCoord block_coord(const Geo& g, int b) {
-  const int per_frame = g.gh * g.gw;
   BlockCoord c;
-  c.t = b / per_frame;
-  const int r = b - c.t * per_frame;
-  c.hb = r / g.gw;
+  c.t = div16(b, g.per_frame_r);
+  const int r = b - c.t * (g.gh * g.gw);
+  c.hb = div16(r, g.gw_r);
   c.wb = r - c.hb * g.gw;
   return c;
 }
