@@ -3,10 +3,12 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 720p]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-nabla_pool -> nabla_mask -> nabla_compact -> nabla_attn_fwd, called through
-the C ABI on torch's current stream, with the fractal flatten applied inside
-the pooling and attention loaders (inputs and output stay in the natural
-[B, heads, T, H, W, d] layout).  Inputs are resident in HBM before timing.
+nabla_pool -> nabla_mask -> nabla_compact -> nabla_transpose_v ->
+nabla_attn_fwd_vt (float32 inputs: nabla_attn_fwd), called through the C ABI
+on torch's current stream, with the fractal flatten applied inside the
+pooling, transpose and attention loaders (inputs and output stay in the
+natural [B, heads, T, H, W, d] layout).  Inputs are resident in HBM before
+timing.
 Prints ONE JSON line (plus progress on stderr).
 """
 from __future__ import annotations
@@ -165,10 +167,18 @@ def main():
     rp = torch.empty((B * h, nb + 1), dtype=torch.int32, device=dev)
     ci = torch.empty((B * h, nb * nb), dtype=torch.int32, device=dev)
     o = torch.empty_like(q)
+    vt_path = cfg.torch_dtype == torch.bfloat16
+    vt = (torch.empty((B, h, nb, d, 64), dtype=q.dtype, device=dev) if vt_path else None)
     scale = 1.0 / math.sqrt(d)
     stream = torch.cuda.current_stream()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+
+    def attention():
+        if vt_path:
+            nabla.nabla_attn_fwd_vt(g, q, k, vt, rp, ci, scale, o, stream)
+        else:
+            nabla.nabla_attn_fwd(g, q, k, v, rp, ci, scale, o, stream)
 
     def step(marks=None):
         if marks is not None:
@@ -176,9 +186,11 @@ def main():
         nabla.nabla_pool(g, q, k, qbar, kbar, stream)
         nabla.nabla_mask(g, qbar, kbar, thr, sta, bits, cnt, None, stream)
         nabla.nabla_compact(g, bits, cnt, rp, ci, stream)
+        if vt_path:
+            nabla.nabla_transpose_v(g, v, vt, stream)
         if marks is not None:
             marks[1].record(stream)
-        nabla.nabla_attn_fwd(g, q, k, v, rp, ci, scale, o, stream)
+        attention()
         if marks is not None:
             marks[2].record(stream)
 
@@ -197,7 +209,7 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    mask_ms = sorted(m[0].elapsed_time(m[1]) for m in marks)
+    mask_ms = sorted(m[0].elapsed_time(m[1]) for m in marks)   # incl. transpose_v
     attn_ms = sorted(m[1].elapsed_time(m[2]) for m in marks)
     attn_avg = sum(attn_ms) / len(attn_ms)
     mask_avg = sum(mask_ms) / len(mask_ms)
@@ -221,6 +233,8 @@ def main():
         "mask": time_call(lambda: nabla.nabla_mask(g, qbar, kbar, thr, sta, bits, cnt, None,
                                                    stream)),
         "compact": time_call(lambda: nabla.nabla_compact(g, bits, cnt, rp, ci, stream)),
+        "transpose_v": (time_call(lambda: nabla.nabla_transpose_v(g, v, vt, stream))
+                        if vt_path else 0.0),
         "attn_fwd": attn_avg,
         "flatten_one_tensor": time_call(lambda: nabla.nabla_flatten(g, q, xb, stream)),
         "unflatten_one_tensor": time_call(lambda: nabla.nabla_unflatten(g, xb, o, stream)),
@@ -260,7 +274,8 @@ def main():
             "thr": thr, "sta": list(sta),
         },
         "roofline": {
-            "kernel": "nabla_attn_fwd (attn_fwd_bf16_kernel)",
+            "kernel": ("nabla_attn_fwd_vt (attn_fwd_bf16_kernel, V^T operands)" if vt_path
+                       else "nabla_attn_fwd"),
             "bound": "mfma",
             "achieved": round(attn_tflops, 2),
             "peak": BF16_PEAK_TFLOPS,

@@ -22,6 +22,7 @@ STATUS = {
 DTYPE_F32, DTYPE_BF16 = 0, 1
 LAYOUT_THW, LAYOUT_BLOCKED = 0, 1
 MAX_BLOCKS = 4096
+WORKSPACE_PARTS = 7
 
 
 class nabla_geom(ctypes.Structure):
@@ -46,6 +47,8 @@ SIGNATURES = {
     "nabla_mask": ([_G, _P, _P, ctypes.c_float, _I32P, _P, _P, _P, _P], ctypes.c_int),
     "nabla_compact": ([_G, _P, _P, _P, _P, _P], ctypes.c_int),
     "nabla_attn_fwd": ([_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
+    "nabla_transpose_v": ([_G, _P, _P, _P], ctypes.c_int),
+    "nabla_attn_fwd_vt": ([_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
     "nabla_forward_workspace_size": ([_G, _SZP, _SZP], ctypes.c_int),
     "nabla_forward": ([_G, _P, _P, _P, ctypes.c_float, _I32P, ctypes.c_float, _P, _P,
                        ctypes.c_size_t, _P], ctypes.c_int),

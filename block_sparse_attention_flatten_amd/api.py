@@ -23,8 +23,9 @@ from ._lib import DTYPE_BF16, DTYPE_F32, LAYOUT_BLOCKED, LAYOUT_THW, nabla_geom
 
 __all__ = [
     "NablaError", "Geometry", "nabla_num_blocks", "nabla_flatten", "nabla_unflatten",
-    "nabla_pool", "nabla_mask", "nabla_compact", "nabla_attn_fwd",
-    "nabla_forward_workspace_size", "nabla_forward", "nabla_status_string", "forward",
+    "nabla_pool", "nabla_mask", "nabla_compact", "nabla_attn_fwd", "nabla_transpose_v",
+    "nabla_attn_fwd_vt", "nabla_forward_workspace_size", "nabla_forward", "nabla_status_string",
+    "forward",
     "LAYOUT_THW", "LAYOUT_BLOCKED",
 ]
 
@@ -200,9 +201,32 @@ def nabla_attn_fwd(g: Geometry, q, k, v, row_ptr, col_idx, scale: float, o, stre
         _ptr(o, "o", shp, g.odtype), _stream(stream)), "nabla_attn_fwd")
 
 
+def vt_shape(g: Geometry) -> Tuple[int, ...]:
+    """Shape of the V^T operand layout [B, heads, nb, d, 64]."""
+    return (g.batch, g.heads, g.nb, g.head_dim, 64)
+
+
+def nabla_transpose_v(g: Geometry, v, vt, stream=None) -> None:
+    _check(_lib.load().nabla_transpose_v(
+        ctypes.byref(g.c()), _ptr(v, "v", g.tensor_shape(), g.dtype),
+        _ptr(vt, "vt", vt_shape(g), g.dtype), _stream(stream)), "nabla_transpose_v")
+
+
+def nabla_attn_fwd_vt(g: Geometry, q, k, vt, row_ptr, col_idx, scale: float, o,
+                      stream=None) -> None:
+    shp = g.tensor_shape()
+    bh = g.batch * g.heads
+    _check(_lib.load().nabla_attn_fwd_vt(
+        ctypes.byref(g.c()), _ptr(q, "q", shp, g.dtype), _ptr(k, "k", shp, g.dtype),
+        _ptr(vt, "vt", vt_shape(g), g.dtype),
+        _ptr(row_ptr, "row_ptr", (bh, g.nb + 1), torch.int32),
+        _ptr(col_idx, "col_idx", (bh, g.nb * g.nb), torch.int32), float(scale),
+        _ptr(o, "o", shp, g.odtype), _stream(stream)), "nabla_attn_fwd_vt")
+
+
 def nabla_forward_workspace_size(g: Geometry) -> Tuple[int, Tuple[int, ...]]:
     size = ctypes.c_size_t(0)
-    offs = (ctypes.c_size_t * 6)()
+    offs = (ctypes.c_size_t * _lib.WORKSPACE_PARTS)()
     _check(_lib.load().nabla_forward_workspace_size(ctypes.byref(g.c()), ctypes.byref(size),
                                                     offs), "nabla_forward_workspace_size")
     return size.value, tuple(offs)

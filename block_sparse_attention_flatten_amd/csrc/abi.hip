@@ -75,18 +75,21 @@ bool scale_ok(float s) { return isfinite(s) && s > 0.0f; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-void workspace_parts(const Geo& g, size_t off[6], size_t* total) {
+constexpr int kWsParts = 7;
+
+void workspace_parts(const Geo& g, bool bf16, size_t off[kWsParts], size_t* total) {
   const size_t bh = (size_t)g.bh, nb = (size_t)g.nb, nw = (nb + 31) / 32;
-  const size_t sizes[6] = {
+  const size_t sizes[kWsParts] = {
       bh * nb * g.d * sizeof(float),        // qbar
       bh * nb * g.d * sizeof(float),        // kbar
       bh * nb * nw * sizeof(uint32_t),      // mask bits
       bh * nb * sizeof(int32_t),            // row counts
       bh * (nb + 1) * sizeof(int32_t),      // row_ptr
       bh * nb * nb * sizeof(int32_t),       // col_idx
+      bf16 ? bh * nb * 64 * g.d * 2 : 0,    // V^T
   };
   size_t at = 0;
-  for (int i = 0; i < 6; ++i) {
+  for (int i = 0; i < kWsParts; ++i) {
     off[i] = at;
     at = align256(at + sizes[i]);
   }
@@ -214,14 +217,42 @@ int nabla_attn_fwd(const nabla_geom* geom, const void* q, const void* k, const v
                                            col_idx, scale, o, as_stream(stream)));
 }
 
+int nabla_transpose_v(const nabla_geom* geom, const void* v, void* vt, void* stream) {
+  Geo g;
+  bool empty;
+  const int st = make_geo(geom, true, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (geom->dtype != NABLA_DTYPE_BF16) return NABLA_E_DTYPE;
+  if (empty) return NABLA_OK;
+  if (v == nullptr || vt == nullptr) return NABLA_E_NULL;
+  return hip_status(nabla::launch_transpose_v(g, v, vt, as_stream(stream)));
+}
+
+int nabla_attn_fwd_vt(const nabla_geom* geom, const void* q, const void* k, const void* vt,
+                      const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
+                      void* stream) {
+  Geo g;
+  bool empty;
+  const int st = make_geo(geom, true, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (geom->dtype != NABLA_DTYPE_BF16) return NABLA_E_DTYPE;
+  if (!scale_ok(scale)) return NABLA_E_SCALE;
+  if (empty) return NABLA_OK;
+  if (q == nullptr || k == nullptr || vt == nullptr || row_ptr == nullptr ||
+      col_idx == nullptr || o == nullptr)
+    return NABLA_E_NULL;
+  return hip_status(nabla::launch_attn_fwd_vt(g, geom->out_dtype == NABLA_DTYPE_BF16, q, k, vt,
+                                              row_ptr, col_idx, scale, o, as_stream(stream)));
+}
+
 int nabla_forward_workspace_size(const nabla_geom* geom, size_t* bytes, size_t* offsets) {
   Geo g;
   bool empty;
   const int st = make_geo(geom, true, &g, &empty);
   if (st != NABLA_OK) return st;
   if (bytes == nullptr) return NABLA_E_NULL;
-  size_t off[6], total;
-  workspace_parts(g, off, &total);
+  size_t off[kWsParts], total;
+  workspace_parts(g, geom->dtype == NABLA_DTYPE_BF16, off, &total);
   *bytes = total;
   if (offsets != nullptr) memcpy(offsets, off, sizeof(off));
   return NABLA_OK;
@@ -242,8 +273,9 @@ int nabla_forward(const nabla_geom* geom, const void* q, const void* k, const vo
   if (empty) return NABLA_OK;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || workspace == nullptr)
     return NABLA_E_NULL;
-  size_t off[6], total;
-  workspace_parts(g, off, &total);
+  const bool bf16 = geom->dtype == NABLA_DTYPE_BF16;
+  size_t off[kWsParts], total;
+  workspace_parts(g, bf16, off, &total);
   if (workspace_bytes < total) return NABLA_E_WORKSPACE;
   char* ws = (char*)workspace;
   float* qbar = (float*)(ws + off[0]);
@@ -253,13 +285,17 @@ int nabla_forward(const nabla_geom* geom, const void* q, const void* k, const vo
   int32_t* rp = (int32_t*)(ws + off[4]);
   int32_t* ci = (int32_t*)(ws + off[5]);
   const hipStream_t s = as_stream(stream);
-  const bool bf16 = geom->dtype == NABLA_DTYPE_BF16;
+  const bool out_bf16 = geom->out_dtype == NABLA_DTYPE_BF16;
   hipError_t e = nabla::launch_pool(g, bf16, q, k, qbar, kbar, s);
   if (e == hipSuccess) e = nabla::launch_mask(g, qbar, kbar, thr, win, bits, cnt, nullptr, s);
   if (e == hipSuccess) e = nabla::launch_compact(g, bits, cnt, rp, ci, s);
-  if (e == hipSuccess)
-    e = nabla::launch_attn_fwd(g, bf16, geom->out_dtype == NABLA_DTYPE_BF16, q, k, v, rp, ci,
-                               scale, o, s);
+  if (bf16) {
+    void* vt = ws + off[6];
+    if (e == hipSuccess) e = nabla::launch_transpose_v(g, v, vt, s);
+    if (e == hipSuccess) e = nabla::launch_attn_fwd_vt(g, out_bf16, q, k, vt, rp, ci, scale, o, s);
+  } else if (e == hipSuccess) {
+    e = nabla::launch_attn_fwd(g, false, false, q, k, v, rp, ci, scale, o, s);
+  }
   return hip_status(e);
 }
 

@@ -80,6 +80,10 @@ struct AttnShape {
   // group: a stride of 8 (mod 32) banks keeps those 4 rows disjoint.
   static constexpr int kStride = D + 8;
   static constexpr int kVStride = D + 16;
+  // V^T tile (d rows x 64 keys) when V comes pre-transposed: a 144-byte row
+  // stride (4 banks mod 32) keeps 8 consecutive rows' 16-byte reads disjoint
+  static constexpr int kVTStride = kN + 8;
+  static constexpr int kVElems = (kN * kVStride > D * kVTStride) ? kN * kVStride : D * kVTStride;
   static constexpr int kThreads = 256;
   static constexpr int kChunks = D / 8;           // 16-byte chunks per token row
   static constexpr int kRowsPerPass = kThreads / kChunks;
@@ -126,7 +130,10 @@ __device__ inline KeptList kept_list(const int32_t* row_ptr, const int32_t* cols
   return l;
 }
 
-template <int D, typename OutT>
+// kVT: V arrives as V^T tiles ([.., nb, d, 64], keys in operand order, see
+// transpose_v.hip) and its operands are plain 16-byte LDS reads; otherwise V
+// is in the Q/K layout and its operands come from transpose loads.
+template <int D, typename OutT, bool kVT>
 __global__ void __launch_bounds__(256, 2)
 attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const int32_t* __restrict__ row_ptr,
@@ -134,7 +141,7 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
                      OutT* __restrict__ O) {
   using A = AttnShape<D>;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[kN * A::kStride];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[kN * A::kVStride];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[A::kVElems];
 
   const int nb = g.nb;
   const int items = pair_items(g);
@@ -197,13 +204,15 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
     const int cv = block_cols_valid(g, bc);
     const __bf16* kb = K + hoff + block_base(g, beta, bc) + ld_chunk * 8;
     const __bf16* vb = V + hoff + block_base(g, beta, bc) + ld_chunk * 8;
+    const __bf16* vtb = V + (head * nb + beta) * (int64_t)(kN * D) + tid * 8;
 #pragma unroll
     for (int p = 0; p < A::kPasses; ++p) {
       const int r = ld_row + p * A::kRowsPerPass;
       const bool ok = (r >> 3) < rv && (r & 7) < cv;
       const int off = ok ? (r >> 3) * row_step + (r & 7) * D : 0;
       kreg[p] = *(const u32x4*)(kb + off);
-      vreg[p] = *(const u32x4*)(vb + off);
+      // V^T tile: d rows x 64 keys, contiguous; chunk tid + 256 p
+      vreg[p] = kVT ? *(const u32x4*)(vtb + p * A::kThreads * 8) : *(const u32x4*)(vb + off);
     }
   };
 
@@ -221,7 +230,12 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
     for (int p = 0; p < A::kPasses; ++p) {
       const int r = ld_row + p * A::kRowsPerPass;
       *(u32x4*)(Ks + r * A::kStride + ld_chunk * 8) = kreg[p];
-      *(u32x4*)(Vs + r * A::kVStride + ld_chunk * 8) = vreg[p];
+      if (kVT) {
+        const int c = tid + p * A::kThreads;   // V^T chunk: row c / 8, keys 8 (c % 8) ..
+        *(u32x4*)(Vs + (c >> 3) * A::kVTStride + (c & 7) * 8) = vreg[p];
+      } else {
+        *(u32x4*)(Vs + r * A::kVStride + ld_chunk * 8) = vreg[p];
+      }
     }
     __syncthreads();
     if (next != INT_MAX) fetch(next);
@@ -304,13 +318,18 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int k0 = 32 * kt + 16 * h + 4 * hl;
-          const __bf16* src = vsrc + k0 * A::kVStride + 32 * dt;
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(src));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(src + 8 * A::kVStride));
-          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          bf16x8 a;
+          if (kVT) {   // V^T row 32dt + jl, stored keys 16(2kt + h) + 8hl .. +7
+            a = *(const bf16x8*)(Vs + (32 * dt + jl) * A::kVTStride + 16 * (2 * kt + h) + 8 * hl);
+          } else {
+            const int k0 = 32 * kt + 16 * h + 4 * hl;
+            const __bf16* src = vsrc + k0 * A::kVStride + 32 * dt;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (__attribute__((address_space(3))) bf16x4*)(src));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (__attribute__((address_space(3))) bf16x4*)(src + 8 * A::kVStride));
+            a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[kt][h], oacc[dt], 0, 0, 0);
         }
       }
@@ -408,15 +427,28 @@ attn_fwd_f32_kernel(const Geo g, const float* __restrict__ Q, const float* __res
   }
 }
 
-template <int D, typename OutT>
+template <int D, typename OutT, bool kVT>
 void launch_bf16(const Geo& g, const void* q, const void* k, const void* v,
                  const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
                  hipStream_t s) {
   const float sl2 = scale * 1.4426950408889634f;   // softmax in base 2
   const int64_t chunk = (pair_items(g) + 7) / 8;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OutT>), dim3((unsigned)(8 * chunk * g.bh)),
-                     dim3(AttnShape<D>::kThreads), 0, s, g, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                     sl2, (OutT*)o);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OutT, kVT>), dim3((unsigned)(8 * chunk * g.bh)),
+                     dim3(AttnShape<D>::kThreads), 0, s, g, (const __bf16*)q, (const __bf16*)k,
+                     (const __bf16*)v, row_ptr, col_idx, sl2, (OutT*)o);
+}
+
+template <bool kVT>
+void launch_bf16_any(const Geo& g, bool out_bf16, const void* q, const void* k, const void* v,
+                     const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
+                     hipStream_t s) {
+  if (g.d == 64) {
+    out_bf16 ? launch_bf16<64, __bf16, kVT>(g, q, k, v, row_ptr, col_idx, scale, o, s)
+             : launch_bf16<64, float, kVT>(g, q, k, v, row_ptr, col_idx, scale, o, s);
+  } else {
+    out_bf16 ? launch_bf16<128, __bf16, kVT>(g, q, k, v, row_ptr, col_idx, scale, o, s)
+             : launch_bf16<128, float, kVT>(g, q, k, v, row_ptr, col_idx, scale, o, s);
+  }
 }
 
 template <int D>
@@ -434,17 +466,18 @@ hipError_t launch_attn_fwd(const Geo& g, bool bf16, bool out_bf16, const void* q
                            const void* v, const int32_t* row_ptr, const int32_t* col_idx,
                            float scale, void* o, hipStream_t s) {
   if (bf16) {
-    if (g.d == 64) {
-      out_bf16 ? launch_bf16<64, __bf16>(g, q, k, v, row_ptr, col_idx, scale, o, s)
-               : launch_bf16<64, float>(g, q, k, v, row_ptr, col_idx, scale, o, s);
-    } else {
-      out_bf16 ? launch_bf16<128, __bf16>(g, q, k, v, row_ptr, col_idx, scale, o, s)
-               : launch_bf16<128, float>(g, q, k, v, row_ptr, col_idx, scale, o, s);
-    }
+    launch_bf16_any<false>(g, out_bf16, q, k, v, row_ptr, col_idx, scale, o, s);
   } else {
     g.d == 64 ? launch_f32<64>(g, q, k, v, row_ptr, col_idx, scale, o, s)
               : launch_f32<128>(g, q, k, v, row_ptr, col_idx, scale, o, s);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_vt(const Geo& g, bool out_bf16, const void* q, const void* k,
+                              const void* vt, const int32_t* row_ptr, const int32_t* col_idx,
+                              float scale, void* o, hipStream_t s) {
+  launch_bf16_any<true>(g, out_bf16, q, k, vt, row_ptr, col_idx, scale, o, s);
   return hipGetLastError();
 }
 

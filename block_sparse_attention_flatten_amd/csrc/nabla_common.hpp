@@ -101,5 +101,9 @@ hipError_t launch_compact(const Geo& g, const uint32_t* bits, const int32_t* cnt
 hipError_t launch_attn_fwd(const Geo& g, bool bf16, bool out_bf16, const void* q, const void* k,
                            const void* v, const int32_t* row_ptr, const int32_t* col_idx,
                            float scale, void* o, hipStream_t s);
+hipError_t launch_transpose_v(const Geo& g, const void* v, void* vt, hipStream_t s);
+hipError_t launch_attn_fwd_vt(const Geo& g, bool out_bf16, const void* q, const void* k,
+                              const void* vt, const int32_t* row_ptr, const int32_t* col_idx,
+                              float scale, void* o, hipStream_t s);
 
 }  // namespace nabla

@@ -16,8 +16,10 @@
  *                                                                  CDF thresholding, hybrid STA
  *   nabla_compact     per-head compressed (CSR) kept-block lists   [LS] sec. 5
  *   nabla_attn_fwd    exact attention on kept N x N token blocks   [GZ] expansion; [LS] sec. 2
+ *   nabla_transpose_v V in the per-block transposed operand layout
+ *   nabla_attn_fwd_vt nabla_attn_fwd reading that layout (faster)
  *   nabla_unflatten   inverse reorder of the output
- *   nabla_forward     pool -> mask -> compact -> attn_fwd in one call
+ *   nabla_forward     pool -> mask -> compact -> (transpose_v) -> attn_fwd in one call
  *
  * Conventions for every entry point
  *   - All pointers except `geom`, `sta` and `bytes`/`offsets` outputs are
@@ -54,6 +56,10 @@
  *   CSR: row_ptr int32 [B*heads, nb + 1] (offsets inside that head's list);
  *        col_idx int32 [B*heads, nb * nb] capacity; head i's list starts at
  *        col_idx + i * nb * nb; kept block indices of a row are ascending.
+ *   V^T (bf16 only): [B, heads, nb, d, 64]; row c of block b holds channel c
+ *        of the block's 64 key slots, in the order that swaps bits 2 and 3 of
+ *        the slot index (positions 0-3, 4-7, 8-11, 12-15 of every 16 hold
+ *        slots 0-3, 8-11, 4-7, 12-15); pad slots are zero.
  */
 #ifndef NABLA_H
 #define NABLA_H
@@ -166,14 +172,28 @@ int nabla_attn_fwd(const nabla_geom* geom, const void* q, const void* k,
                    const void* v, const int32_t* row_ptr, const int32_t* col_idx,
                    float scale, void* o, void* stream);
 
+/* V in the V^T layout above (bf16 inputs only): the attention kernel reads
+ * it as matrix-core operands with plain 16-byte loads instead of transposing
+ * V on chip.  v in geom's layout; vt [B, heads, nb, d, 64].  Bit-exact copy. */
+int nabla_transpose_v(const nabla_geom* geom, const void* v, void* vt, void* stream);
+
+/* nabla_attn_fwd with V given as nabla_transpose_v's output (bf16 inputs
+ * only).  Same arguments otherwise; the result is bit-identical to
+ * nabla_attn_fwd's. */
+int nabla_attn_fwd_vt(const nabla_geom* geom, const void* q, const void* k,
+                      const void* vt, const int32_t* row_ptr, const int32_t* col_idx,
+                      float scale, void* o, void* stream);
+
 /* Workspace for nabla_forward and the byte offsets of its parts, in order:
  * offsets[0] qbar, [1] kbar, [2] mask_bits, [3] row_count, [4] row_ptr,
- * [5] col_idx (see the layouts above); `offsets` (host, 6 entries) may be
- * NULL.  Every part is 256-byte aligned. */
+ * [5] col_idx, [6] V^T (bf16 inputs; empty for float32) (see the layouts
+ * above); `offsets` (host, 7 entries) may be NULL.  Every part is 256-byte
+ * aligned. */
 int nabla_forward_workspace_size(const nabla_geom* geom, size_t* bytes, size_t* offsets);
 
-/* One NABLA attention call: nabla_pool, nabla_mask, nabla_compact and
- * nabla_attn_fwd in sequence on `stream`, with the intermediates in
+/* One NABLA attention call: nabla_pool, nabla_mask, nabla_compact and the
+ * attention (bf16: nabla_transpose_v + nabla_attn_fwd_vt; float32:
+ * nabla_attn_fwd) in sequence on `stream`, with the intermediates in
  * `workspace` (device memory of at least nabla_forward_workspace_size bytes,
  * caller-owned; its parts can be read back after the call). */
 int nabla_forward(const nabla_geom* geom, const void* q, const void* k, const void* v,

@@ -81,6 +81,12 @@ def test_argument_validation():
                                   None) == -11
     assert lib.nabla_attn_fwd(ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, None, 0.1, FAKE, None) == -1
     assert lib.nabla_compact(ctypes.byref(g), FAKE, FAKE, FAKE, None, None) == -1
+    assert lib.nabla_transpose_v(ctypes.byref(g), FAKE, None, None) == -1
+    assert lib.nabla_transpose_v(ctypes.byref(G(dtype=0, out_dtype=0)), FAKE, FAKE, None) == -3
+    assert lib.nabla_attn_fwd_vt(ctypes.byref(G(dtype=0, out_dtype=0)), FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, 0.1, FAKE, None) == -3
+    assert lib.nabla_attn_fwd_vt(ctypes.byref(g), FAKE, FAKE, None, FAKE, FAKE, 0.1, FAKE,
+                                 None) == -1
     assert lib.nabla_flatten(ctypes.byref(g), None, FAKE, None) == -1
     assert lib.nabla_unflatten(ctypes.byref(g), FAKE, None, None) == -1
     size = ctypes.c_size_t(0)
@@ -113,13 +119,14 @@ def test_workspace_layout_and_block_count():
     assert lib.nabla_num_blocks(ctypes.byref(g), ctypes.byref(nb)) == 0
     assert nb.value == 1260
     size = ctypes.c_size_t(0)
-    offs = (ctypes.c_size_t * 6)()
+    offs = (ctypes.c_size_t * 7)()
     assert lib.nabla_forward_workspace_size(ctypes.byref(g), ctypes.byref(size), offs) == 0
     o = list(offs)
     assert o[0] == 0 and all(x % 256 == 0 for x in o) and o == sorted(o)
     bh, n, d = 40, 1260, 128
     assert o[1] >= bh * n * d * 4 and o[2] - o[1] >= bh * n * d * 4
-    assert size.value - o[5] >= bh * n * n * 4
+    assert o[6] - o[5] >= bh * n * n * 4
+    assert size.value - o[6] >= bh * n * 64 * d * 2      # V^T for bf16 inputs
     # Long: 41 x 45 x 80 -> 2460 blocks; 480p: 21 x 30 x 52 -> 21 x 4 x 7
     assert lib.nabla_num_blocks(ctypes.byref(G(T=41, H=45, W=80)), ctypes.byref(nb)) == 0
     assert nb.value == 2460

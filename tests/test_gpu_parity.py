@@ -195,7 +195,8 @@ def test_compact_against_oracle_csr():
 
 
 def test_forward_entry_point_matches_stepwise():
-    """nabla_forward (one call) == the four entry points called one by one, bit for bit."""
+    """nabla_forward (one call, V^T path for bf16) == the entry points called
+    one by one (on-chip transposing attention), bit for bit."""
     cfg = synth.config("small", heads=3, T=3, H=21, W=30, thr=0.75, sta=(3, 3, 3))
     q, k, v = synth.make_qkv(cfg, device="cuda")
     step = run_pipeline(cfg, q, k, v, out_dtype=torch.bfloat16)
@@ -237,3 +238,38 @@ def test_empty_batch_is_a_no_op():
     res = nabla.forward(q, q, q, 0.5, (3, 3, 3))
     torch.cuda.synchronize()
     assert res.o.numel() == 0
+
+
+def _vt_reference(v: torch.Tensor, cfg) -> np.ndarray:
+    """V^T layout from its definition: block b, row c = channel c of the 64 key
+    slots, slot order with bits 2 and 3 of the position swapped; pads zero."""
+    og = ogeom(cfg)
+    vb = O.flatten(v.cpu().view(torch.int16).numpy(), og)          # [B, h, nb, 64, d]
+    pos = np.arange(64)
+    key = (pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1)
+    return np.ascontiguousarray(np.swapaxes(vb[..., key, :], -1, -2))   # [B, h, nb, d, 64]
+
+
+def test_transpose_v_and_attn_fwd_vt(case):
+    name, cfg, q, k, v = case
+    if q.dtype != torch.bfloat16:
+        pytest.skip("the V^T path is bf16-only")
+    g = geom_of(cfg)
+    vt = torch.full((cfg.batch, cfg.heads, g.nb, cfg.head_dim, 64), 5.0, dtype=v.dtype,
+                    device="cuda")
+    nabla.nabla_transpose_v(g, v, vt)
+    torch.cuda.synchronize()
+    assert np.array_equal(vt.cpu().view(torch.int16).numpy(), _vt_reference(v, cfg))
+    # the attention reading V^T is bit-identical to the one transposing on chip
+    res = run_pipeline(cfg, q, k, v, out_dtype=torch.float32)
+    for odt in (torch.float32, torch.bfloat16):
+        gg = geom_of(cfg, out_dtype=odt)
+        o_vt = torch.empty(q.shape, dtype=odt, device="cuda")
+        o_tr = torch.empty(q.shape, dtype=odt, device="cuda")
+        nabla.nabla_attn_fwd_vt(gg, q, k, vt, res["rp"], res["ci"], 1.0 / math.sqrt(cfg.head_dim),
+                                o_vt)
+        nabla.nabla_attn_fwd(gg, q, k, v, res["rp"], res["ci"], 1.0 / math.sqrt(cfg.head_dim),
+                             o_tr)
+        torch.cuda.synchronize()
+        iv = torch.int32 if odt == torch.float32 else torch.int16
+        assert torch.equal(o_vt.view(iv), o_tr.view(iv)), f"{name}: V^T path differs ({odt})"
