@@ -72,6 +72,32 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
 
 
+def traffic_record(workload_is_default):
+    """HBM bytes per launch of the attention kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the 720p workload.  Valid only
+    while the kernel source hashes to the value recorded there and the
+    workload is that default one; otherwise None."""
+    import hashlib
+    import re
+    if not workload_is_default:
+        return None
+    path = os.path.join(ROOT, "profiles", "attn_fwd_720p.md")
+    csrc = os.path.join(ROOT, "block_sparse_attention_flatten_amd", "csrc")
+    try:
+        text = open(path).read()
+        src = b"".join(open(os.path.join(csrc, n), "rb").read()
+                       for n in ("attn_fwd.hip", "nabla_common.hpp"))
+    except OSError:
+        return None
+    m = re.search(r"<!-- traffic-record: (\{.*?\}) -->", text)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_sha256_16") != hashlib.sha256(src).hexdigest()[:16]:
+        return None
+    return float(rec["traffic_bytes"])
+
+
 def algorithmic_bytes(cfg, nb, nnz_total):
     """HBM bytes each mask-construction stage must move at minimum."""
     bh = cfg.batch * cfg.heads
@@ -281,7 +307,9 @@ def main():
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic_record(vt_path and cfg.name == "720p" and args.heads is None
+                                      and args.thr is None and args.sta is None),
+            "traffic_unit": "bytes per launch (HBM, counter-calibrated)",
             "work_per_launch": f"{nnz} kept 64x64 block pairs x 4*64*64*{d} flop = "
                                f"{kept_flops / 1e12:.3f} TFLOP",
             "avg_launch_ms": round(attn_avg, 4),
