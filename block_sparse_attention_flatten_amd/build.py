@@ -25,6 +25,12 @@ HIP_FLAGS = [
 ]
 _NOISE = "is not a recognized feature for this target"
 
+# Per-source extras.  The pipelined attention kernel takes row maxima of
+# matrix-core results, which are never NaN for finite inputs; without NaN
+# semantics the compiler drops the canonicalising moves it would otherwise
+# put in front of every v_max.
+FILE_FLAGS = {"attn_fwd_vt.hip": ["-fno-honor-nans"]}
+
 
 def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
@@ -57,7 +63,8 @@ def build_library(out: str = LIB, verbose: bool = False) -> str:
     jobs = []
     for src in sources():
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        jobs.append((obj, [cc, *HIP_FLAGS, *inc, "-c", src, "-o", obj]))
+        extra = FILE_FLAGS.get(os.path.basename(src), [])
+        jobs.append((obj, [cc, *HIP_FLAGS, *extra, *inc, "-c", src, "-o", obj]))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         list(ex.map(lambda j: _run(j[1], verbose), jobs))
     tmp = out + ".tmp"

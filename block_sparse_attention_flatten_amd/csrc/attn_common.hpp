@@ -1,0 +1,59 @@
+// Pieces shared by the bf16 attention kernels: the pair work items, the
+// workgroup -> (head, item) order, and the output store.
+#pragma once
+
+#include <limits.h>
+
+#include "nabla_common.hpp"
+
+namespace nabla {
+
+// Pair work items of one head: item p -> query blocks (a, b), b = -1 when a
+// has no partner.  Pairs are (t, hb, wb) and (t + 1, hb, wb) for even t; when
+// T is odd the last frame pairs (hb, wb) with (hb, wb + 1) for even wb.
+__host__ __device__ inline int pair_items(const Geo& g) {
+  const int pf = g.gh * g.gw;
+  return (g.T >> 1) * pf + ((g.T & 1) ? g.gh * ((g.gw + 1) >> 1) : 0);
+}
+__device__ inline void pair_of(const Geo& g, int p, int* a, int* b) {
+  const int pf = g.gh * g.gw;
+  const int nfull = (g.T >> 1) * pf;
+  if (p < nfull) {
+    const int t2 = p / pf;
+    *a = 2 * t2 * pf + (p - t2 * pf);
+    *b = *a + pf;
+    return;
+  }
+  const int q = p - nfull, hw = (g.gw + 1) >> 1;
+  const int hb = q / hw, wp = q - hb * hw;
+  *a = (g.T - 1) * pf + hb * g.gw + 2 * wp;
+  *b = 2 * wp + 1 < g.gw ? *a + 1 : -1;
+}
+
+// Workgroup id -> (head, pair item).  Workgroups are dispatched in id order,
+// round-robin over the 8 XCDs (XCD = id % 8).  Each head's items are cut into
+// 8 contiguous chunks and XCD x takes chunk x of every head in turn: all XCDs
+// work on the same head at any time and each XCD's L2 sees one compact
+// spatial region whose kept lists overlap.  False for padding ids.
+__device__ inline bool xcd_item(int bid, int items, int chunk, int64_t* head, int* item) {
+  const int x = bid & 7, i = bid >> 3;
+  const int h = i / chunk;
+  const int it = x * chunk + (i - h * chunk);
+  *head = h;
+  *item = it;
+  return it < items;
+}
+
+template <typename OutT>
+__device__ inline void store4(OutT* dst, float a, float b, float c, float d);
+template <>
+__device__ inline void store4<__bf16>(__bf16* dst, float a, float b, float c, float d) {
+  bf16x4 v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};   // round to nearest even
+  *(bf16x4*)dst = v;
+}
+template <>
+__device__ inline void store4<float>(float* dst, float a, float b, float c, float d) {
+  *(f32x4*)dst = f32x4{a, b, c, d};
+}
+
+}  // namespace nabla

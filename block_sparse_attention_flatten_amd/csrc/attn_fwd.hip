@@ -4,8 +4,9 @@
 // lsdiaocha.cn article, sec. 2 step 3: each kept reduced entry stands for a
 // whole N x N block computed exactly).
 //
-// bf16 path, gfx950 matrix cores.  The kernel is bound by how often a K/V tile
-// must come from beyond the XCD's L2, so one workgroup serves TWO query blocks
+// bf16 path with V in the Q/K layout (nabla_attn_fwd), gfx950 matrix cores.
+// The pipelined kernel for V given as V^T tiles (attn_fwd_vt.hip) is the fast
+// path; this one needs no V^T pass.  One workgroup serves TWO query blocks
 // that see similar keys -- the same 8x8 patch in two consecutive frames (an
 // odd last frame pairs horizontal neighbours) -- and walks the merged,
 // ascending union of their kept lists: every K/V tile in the union is fetched
@@ -28,49 +29,11 @@
 //
 // fp32 path: a plain kernel (one thread per query, fp32 FMA, K/V tiles in
 // LDS) used for float32 inputs.
-#include <limits.h>
-
-#include "nabla_common.hpp"
+#include "attn_common.hpp"
 
 namespace nabla {
 
 namespace {
-
-// Pair work items of one head: item p -> query blocks (a, b), b = -1 when a
-// has no partner.  Pairs are (t, hb, wb) and (t + 1, hb, wb) for even t; when
-// T is odd the last frame pairs (hb, wb) with (hb, wb + 1) for even wb.
-__host__ __device__ inline int pair_items(const Geo& g) {
-  const int pf = g.gh * g.gw;
-  return (g.T >> 1) * pf + ((g.T & 1) ? g.gh * ((g.gw + 1) >> 1) : 0);
-}
-__device__ inline void pair_of(const Geo& g, int p, int* a, int* b) {
-  const int pf = g.gh * g.gw;
-  const int nfull = (g.T >> 1) * pf;
-  if (p < nfull) {
-    const int t2 = p / pf;
-    *a = 2 * t2 * pf + (p - t2 * pf);
-    *b = *a + pf;
-    return;
-  }
-  const int q = p - nfull, hw = (g.gw + 1) >> 1;
-  const int hb = q / hw, wp = q - hb * hw;
-  *a = (g.T - 1) * pf + hb * g.gw + 2 * wp;
-  *b = 2 * wp + 1 < g.gw ? *a + 1 : -1;
-}
-
-// Workgroup id -> (head, pair item).  Workgroups are dispatched in id order,
-// round-robin over the 8 XCDs (XCD = id % 8).  Each head's items are cut into
-// 8 contiguous chunks and XCD x takes chunk x of every head in turn: all XCDs
-// work on the same head at any time and each XCD's L2 sees one compact
-// spatial region whose kept lists overlap.  False for padding ids.
-__device__ inline bool xcd_item(int bid, int items, int chunk, int64_t* head, int* item) {
-  const int x = bid & 7, i = bid >> 3;
-  const int h = i / chunk;
-  const int it = x * chunk + (i - h * chunk);
-  *head = h;
-  *item = it;
-  return it < items;
-}
 
 template <int D>
 struct AttnShape {
@@ -80,10 +43,6 @@ struct AttnShape {
   // group: a stride of 8 (mod 32) banks keeps those 4 rows disjoint.
   static constexpr int kStride = D + 8;
   static constexpr int kVStride = D + 16;
-  // V^T tile (d rows x 64 keys) when V comes pre-transposed: a 144-byte row
-  // stride (4 banks mod 32) keeps 8 consecutive rows' 16-byte reads disjoint
-  static constexpr int kVTStride = kN + 8;
-  static constexpr int kVElems = (kN * kVStride > D * kVTStride) ? kN * kVStride : D * kVTStride;
   static constexpr int kThreads = 256;
   static constexpr int kChunks = D / 8;           // 16-byte chunks per token row
   static constexpr int kRowsPerPass = kThreads / kChunks;
@@ -91,18 +50,6 @@ struct AttnShape {
   static constexpr int kSteps = D / 16;           // k-steps of S^T = K Q^T
   static constexpr int kDTiles = D / 32;          // 32-row tiles of O^T
 };
-
-template <typename OutT>
-__device__ inline void store4(OutT* dst, float a, float b, float c, float d);
-template <>
-__device__ inline void store4<__bf16>(__bf16* dst, float a, float b, float c, float d) {
-  bf16x4 v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};   // round to nearest even
-  *(bf16x4*)dst = v;
-}
-template <>
-__device__ inline void store4<float>(float* dst, float a, float b, float c, float d) {
-  *(f32x4*)dst = f32x4{a, b, c, d};
-}
 
 // Ascending kept list of one query block, read through the scalar cache (the
 // constant address space makes these uniform reads scalar loads); entries
@@ -130,10 +77,8 @@ __device__ inline KeptList kept_list(const int32_t* row_ptr, const int32_t* cols
   return l;
 }
 
-// kVT: V arrives as V^T tiles ([.., nb, d, 64], keys in operand order, see
-// transpose_v.hip) and its operands are plain 16-byte LDS reads; otherwise V
-// is in the Q/K layout and its operands come from transpose loads.
-template <int D, typename OutT, bool kVT>
+// V is in the Q/K layout; its matrix-core operands come from transpose loads.
+template <int D, typename OutT>
 __global__ void __launch_bounds__(256, 2)
 attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const int32_t* __restrict__ row_ptr,
@@ -141,7 +86,7 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
                      OutT* __restrict__ O) {
   using A = AttnShape<D>;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[kN * A::kStride];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[A::kVElems];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[kN * A::kVStride];
 
   const int nb = g.nb;
   const int items = pair_items(g);
@@ -204,15 +149,13 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
     const int cv = block_cols_valid(g, bc);
     const __bf16* kb = K + hoff + block_base(g, beta, bc) + ld_chunk * 8;
     const __bf16* vb = V + hoff + block_base(g, beta, bc) + ld_chunk * 8;
-    const __bf16* vtb = V + (head * nb + beta) * (int64_t)(kN * D) + tid * 8;
 #pragma unroll
     for (int p = 0; p < A::kPasses; ++p) {
       const int r = ld_row + p * A::kRowsPerPass;
       const bool ok = (r >> 3) < rv && (r & 7) < cv;
       const int off = ok ? (r >> 3) * row_step + (r & 7) * D : 0;
       kreg[p] = *(const u32x4*)(kb + off);
-      // V^T tile: d rows x 64 keys, contiguous; chunk tid + 256 p
-      vreg[p] = kVT ? *(const u32x4*)(vtb + p * A::kThreads * 8) : *(const u32x4*)(vb + off);
+      vreg[p] = *(const u32x4*)(vb + off);
     }
   };
 
@@ -230,27 +173,37 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
     for (int p = 0; p < A::kPasses; ++p) {
       const int r = ld_row + p * A::kRowsPerPass;
       *(u32x4*)(Ks + r * A::kStride + ld_chunk * 8) = kreg[p];
-      if (kVT) {
-        const int c = tid + p * A::kThreads;   // V^T chunk: row c / 8, keys 8 (c % 8) ..
-        *(u32x4*)(Vs + (c >> 3) * A::kVTStride + (c & 7) * 8) = vreg[p];
-      } else {
-        *(u32x4*)(Vs + r * A::kVStride + ld_chunk * 8) = vreg[p];
-      }
+      *(u32x4*)(Vs + r * A::kVStride + ld_chunk * 8) = vreg[p];
     }
     __syncthreads();
     if (next != INT_MAX) fetch(next);
     if (!(grp == 0 ? in_a : in_b)) continue;   // wavefront-uniform: not a kept block of ours
 
     // ---- S^T (64 keys x 32 queries) ----
+    // Operand reads are issued ahead of the matrix instructions that use them
+    // (all of key tile 0, then one of key tile 1 per instruction of tile 0),
+    // so LDS latency overlaps matrix work instead of stalling every
+    // instruction; the scheduling-group barriers at the end pin that order.
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    bf16x8 ka[A::kSteps], kb2[A::kSteps];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int s = 0; s < A::kSteps; ++s)
+      ka[s] = *(const bf16x8*)(Ks + jl * A::kStride + 16 * s + 8 * hl);
 #pragma unroll
-      for (int s = 0; s < A::kSteps; ++s) {
-        const bf16x8 a = *(const bf16x8*)(Ks + (32 * kt + jl) * A::kStride + 16 * s + 8 * hl);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[s], sacc[kt], 0, 0, 0);
-      }
+    for (int s = 0; s < A::kSteps; ++s) {
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qop[s], sacc[0], 0, 0, 0);
+      kb2[s] = *(const bf16x8*)(Ks + (32 + jl) * A::kStride + 16 * s + 8 * hl);
     }
+#pragma unroll
+    for (int s = 0; s < A::kSteps; ++s)
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb2[s], qop[s], sacc[1], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, A::kSteps, 0);
+#pragma unroll
+    for (int s = 0; s < A::kSteps; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, A::kSteps, 0);
     // element r of sacc[kt] is key 32kt + 8(r/4) + 4hl + (r%4) of this lane's query
     const BlockCoord bc = block_coord(g, beta);
     const int rv = block_rows_valid(g, bc);
@@ -306,31 +259,29 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
       }
     }
     // ---- O^T (d x 32 queries) += V^T P^T ----
-    // A operand (V^T rows d = 32dt + lane%32, keys k0..k0+3, k0+8..k0+11 with
-    // k0 = 32kt + 16h + 4hl) straight from the row-major V tile with two
-    // transpose loads: in each 16-lane group, lane i receives element i%4 of
-    // the 4-element rows addressed by lanes 4e + i/4 (e = 0..3), so lane s of
-    // the group addresses key k0 + s/4 (+8), columns d0 + 4(s%4) .. +3.
-    const __bf16* vsrc = Vs + ((lane & 15) >> 2) * A::kVStride + (lane & 16) + 4 * (lane & 3);
+    {
+      // A operand (V^T rows d = 32dt + lane%32, keys k0..k0+3, k0+8..k0+11
+      // with k0 = 32kt + 16h + 4hl) straight from the row-major V tile with
+      // two transpose loads: in each 16-lane group, lane i receives element
+      // i%4 of the 4-element rows addressed by lanes 4e + i/4 (e = 0..3), so
+      // lane s of the group addresses key k0 + s/4 (+8), columns
+      // d0 + 4(s%4) .. +3.
+      const __bf16* vsrc = Vs + ((lane & 15) >> 2) * A::kVStride + (lane & 16) + 4 * (lane & 3);
 #pragma unroll
-    for (int dt = 0; dt < A::kDTiles; ++dt) {
+      for (int dt = 0; dt < A::kDTiles; ++dt) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          bf16x8 a;
-          if (kVT) {   // V^T row 32dt + jl, stored keys 16(2kt + h) + 8hl .. +7
-            a = *(const bf16x8*)(Vs + (32 * dt + jl) * A::kVTStride + 16 * (2 * kt + h) + 8 * hl);
-          } else {
+          for (int h = 0; h < 2; ++h) {
             const int k0 = 32 * kt + 16 * h + 4 * hl;
             const __bf16* src = vsrc + k0 * A::kVStride + 32 * dt;
             const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                 (__attribute__((address_space(3))) bf16x4*)(src));
             const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                 (__attribute__((address_space(3))) bf16x4*)(src + 8 * A::kVStride));
-            a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[kt][h], oacc[dt], 0, 0, 0);
           }
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[kt][h], oacc[dt], 0, 0, 0);
         }
       }
     }
@@ -427,27 +378,26 @@ attn_fwd_f32_kernel(const Geo g, const float* __restrict__ Q, const float* __res
   }
 }
 
-template <int D, typename OutT, bool kVT>
+template <int D, typename OutT>
 void launch_bf16(const Geo& g, const void* q, const void* k, const void* v,
                  const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
                  hipStream_t s) {
   const float sl2 = scale * 1.4426950408889634f;   // softmax in base 2
   const int64_t chunk = (pair_items(g) + 7) / 8;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OutT, kVT>), dim3((unsigned)(8 * chunk * g.bh)),
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OutT>), dim3((unsigned)(8 * chunk * g.bh)),
                      dim3(AttnShape<D>::kThreads), 0, s, g, (const __bf16*)q, (const __bf16*)k,
                      (const __bf16*)v, row_ptr, col_idx, sl2, (OutT*)o);
 }
 
-template <bool kVT>
 void launch_bf16_any(const Geo& g, bool out_bf16, const void* q, const void* k, const void* v,
                      const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
                      hipStream_t s) {
   if (g.d == 64) {
-    out_bf16 ? launch_bf16<64, __bf16, kVT>(g, q, k, v, row_ptr, col_idx, scale, o, s)
-             : launch_bf16<64, float, kVT>(g, q, k, v, row_ptr, col_idx, scale, o, s);
+    out_bf16 ? launch_bf16<64, __bf16>(g, q, k, v, row_ptr, col_idx, scale, o, s)
+             : launch_bf16<64, float>(g, q, k, v, row_ptr, col_idx, scale, o, s);
   } else {
-    out_bf16 ? launch_bf16<128, __bf16, kVT>(g, q, k, v, row_ptr, col_idx, scale, o, s)
-             : launch_bf16<128, float, kVT>(g, q, k, v, row_ptr, col_idx, scale, o, s);
+    out_bf16 ? launch_bf16<128, __bf16>(g, q, k, v, row_ptr, col_idx, scale, o, s)
+             : launch_bf16<128, float>(g, q, k, v, row_ptr, col_idx, scale, o, s);
   }
 }
 
@@ -466,7 +416,7 @@ hipError_t launch_attn_fwd(const Geo& g, bool bf16, bool out_bf16, const void* q
                            const void* v, const int32_t* row_ptr, const int32_t* col_idx,
                            float scale, void* o, hipStream_t s) {
   if (bf16) {
-    launch_bf16_any<false>(g, out_bf16, q, k, v, row_ptr, col_idx, scale, o, s);
+    launch_bf16_any(g, out_bf16, q, k, v, row_ptr, col_idx, scale, o, s);
   } else {
     g.d == 64 ? launch_f32<64>(g, q, k, v, row_ptr, col_idx, scale, o, s)
               : launch_f32<128>(g, q, k, v, row_ptr, col_idx, scale, o, s);
@@ -474,11 +424,5 @@ hipError_t launch_attn_fwd(const Geo& g, bool bf16, bool out_bf16, const void* q
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fwd_vt(const Geo& g, bool out_bf16, const void* q, const void* k,
-                              const void* vt, const int32_t* row_ptr, const int32_t* col_idx,
-                              float scale, void* o, hipStream_t s) {
-  launch_bf16_any<true>(g, out_bf16, q, k, vt, row_ptr, col_idx, scale, o, s);
-  return hipGetLastError();
-}
 
 }  // namespace nabla
