@@ -25,7 +25,7 @@ __all__ = [
     "NablaError", "Geometry", "nabla_num_blocks", "nabla_flatten", "nabla_unflatten",
     "nabla_pool", "nabla_mask", "nabla_compact", "nabla_attn_fwd", "nabla_transpose_v",
     "nabla_attn_fwd_vt", "nabla_forward_workspace_size", "nabla_forward", "nabla_status_string",
-    "forward",
+    "forward", "vt_shape",
     "LAYOUT_THW", "LAYOUT_BLOCKED",
 ]
 

@@ -49,11 +49,13 @@ def tol(dtype: torch.dtype):
 
 
 def run_pipeline(cfg: synth.Config, q, k, v, layout=nabla.LAYOUT_THW, thr=None, sta=None,
-                 out_dtype=torch.float32, also_bf16=False):
-    """Run pool -> mask -> compact -> attn through the C ABI, one entry point
-    at a time (the launch sequence bench.py times).  The output is float32 by
-    default (the kernel's result before any rounding to bf16); with
-    ``also_bf16`` the attention is run a second time writing bf16 (o_bf16)."""
+                 out_dtype=torch.float32, also_bf16=False, attn="vt"):
+    """Run pool -> mask -> compact -> attention through the C ABI, one entry
+    point at a time.  For bf16 inputs the attention is, by default, the launch
+    sequence bench.py times (nabla_transpose_v + nabla_attn_fwd_vt); attn="tr"
+    selects nabla_attn_fwd.  The output is float32 by default (the kernel's
+    result before any rounding to bf16); with ``also_bf16`` the attention is
+    run a second time writing bf16 (o_bf16)."""
     g = geom_of(cfg, layout, out_dtype)
     thr = cfg.thr if thr is None else thr
     sta = cfg.sta if sta is None else sta
@@ -70,12 +72,24 @@ def run_pipeline(cfg: synth.Config, q, k, v, layout=nabla.LAYOUT_THW, thr=None, 
     nabla.nabla_pool(g, q, k, qbar, kbar)
     nabla.nabla_mask(g, qbar, kbar, thr, sta, bits, cnt, abits)
     nabla.nabla_compact(g, bits, cnt, rp, ci)
-    nabla.nabla_attn_fwd(g, q, k, v, rp, ci, 1.0 / math.sqrt(d), o)
+    use_vt = attn == "vt" and q.dtype == torch.bfloat16
+    vt = None
+    if use_vt:
+        vt = torch.empty(nabla.vt_shape(g), dtype=q.dtype, device=dev)
+        nabla.nabla_transpose_v(g, v, vt)
+
+    def attention(geom, out):
+        if use_vt:
+            nabla.nabla_attn_fwd_vt(geom, q, k, vt, rp, ci, 1.0 / math.sqrt(d), out)
+        else:
+            nabla.nabla_attn_fwd(geom, q, k, v, rp, ci, 1.0 / math.sqrt(d), out)
+
+    attention(g, o)
     out = dict(g=g, qbar=qbar, kbar=kbar, bits=bits, abits=abits, cnt=cnt, rp=rp, ci=ci, o=o)
     if also_bf16 and q.dtype == torch.bfloat16:
         gb = geom_of(cfg, layout, torch.bfloat16)
         ob = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
-        nabla.nabla_attn_fwd(gb, q, k, v, rp, ci, 1.0 / math.sqrt(d), ob)
+        attention(gb, ob)
         out["o_bf16"] = ob
     torch.cuda.synchronize()
     return out

@@ -154,9 +154,15 @@ def test_attention_with_oracle_masks(case):
             p_, c_ = O.to_csr(masks[b][h])
             rp[b * cfg.heads + h] = p_
             ci[b * cfg.heads + h, :len(c_)] = c_
-    o = torch.empty(q.shape, dtype=torch.float32, device="cuda")
-    nabla.nabla_attn_fwd(g, q, k, v, torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda(),
-                         1.0 / math.sqrt(cfg.head_dim), o)
+    rp_d, ci_d = torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda()
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    outs = {"attn_fwd": torch.empty(q.shape, dtype=torch.float32, device="cuda")}
+    nabla.nabla_attn_fwd(g, q, k, v, rp_d, ci_d, scale, outs["attn_fwd"])
+    if q.dtype == torch.bfloat16:
+        vt = torch.empty(nabla.vt_shape(g), dtype=q.dtype, device="cuda")
+        nabla.nabla_transpose_v(g, v, vt)
+        outs["attn_fwd_vt"] = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        nabla.nabla_attn_fwd_vt(g, q, k, vt, rp_d, ci_d, scale, outs["attn_fwd_vt"])
     torch.cuda.synchronize()
     for b in range(cfg.batch):
         for h in range(cfg.heads):
@@ -164,7 +170,9 @@ def test_attention_with_oracle_masks(case):
                                           O.flatten(f64(v[b, h]), og), masks[b][h],
                                           O.valid_tokens(og))
             got = O.unflatten(ob, og)
-            check_output(f64(o[b, h]), got, cfg.torch_dtype, f"{name} random-mask b{b} h{h}")
+            for which, o in outs.items():
+                check_output(f64(o[b, h]), got, cfg.torch_dtype,
+                             f"{name} random-mask {which} b{b} h{h}")
 
 
 def test_compact_against_oracle_csr():
@@ -199,7 +207,7 @@ def test_forward_entry_point_matches_stepwise():
     one by one (on-chip transposing attention), bit for bit."""
     cfg = synth.config("small", heads=3, T=3, H=21, W=30, thr=0.75, sta=(3, 3, 3))
     q, k, v = synth.make_qkv(cfg, device="cuda")
-    step = run_pipeline(cfg, q, k, v, out_dtype=torch.bfloat16)
+    step = run_pipeline(cfg, q, k, v, out_dtype=torch.bfloat16, attn="tr")
     res = nabla.forward(q, k, v, cfg.thr, cfg.sta)
     torch.cuda.synchronize()
     assert torch.equal(res.o.view(torch.int16), step["o"].view(torch.int16))
