@@ -2,8 +2,9 @@
 // gist.science, Methodology: reduced attention, CDF thresholding, hybrid
 // integration with STA; lsdiaocha.cn article, sec. 2 step 2 and sec. 4).
 //
-// One workgroup (4 wavefronts) handles R = 16 (or 8) consecutive query-block
-// rows of one head:
+// One workgroup of R wavefronts handles R = 16 (or 8) consecutive
+// query-block rows of one head (the R x nb score tile fills up to ~80 KB of
+// LDS, so one wavefront per row keeps several wavefronts per SIMD busy):
 //   1. scores s[r][c] = qbar_r . kbar_c / sqrt(d) for all c, on fp32 matrix
 //      cores (v_mfma_f32_16x16x4f32), staged in LDS;
 //   2. one wavefront per row: softmax numerators e_c = exp(s_c - max) in
@@ -23,22 +24,48 @@ namespace nabla {
 
 namespace {
 
-constexpr int kWaves = 4;
-
-__device__ inline float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+// Wavefront reductions on the DPP network (no LDS round trips): row-local
+// butterflies leave every lane of a 16-lane row holding the row's result,
+// row_bcast:15 / row_bcast:31 fold the rows into lane 63, which is read out
+// as a wavefront-uniform value.
+template <int kCtrl, int kRowMask, typename T>
+__device__ inline T dpp_src(T x) {
+  return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl,
+                                                           kRowMask, 0xF, false));
 }
-__device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
+template <typename T, typename Op>
+__device__ inline T wave_reduce(T x, Op op) {
+  x = op(x, dpp_src<0xB1, 0xF>(x));    // quad_perm [1,0,3,2]
+  x = op(x, dpp_src<0x4E, 0xF>(x));    // quad_perm [2,3,0,1]
+  x = op(x, dpp_src<0x141, 0xF>(x));   // row_half_mirror
+  x = op(x, dpp_src<0x140, 0xF>(x));   // row_mirror
+  x = op(x, dpp_src<0x142, 0xA>(x));   // row_bcast:15 -> rows 1, 3
+  x = op(x, dpp_src<0x143, 0xC>(x));   // row_bcast:31 -> rows 2, 3
+  return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+__device__ inline float wave_sum(float x) {
+  return wave_reduce(x, [](float a, float b) { return a + b; });
 }
 __device__ inline int wave_sum_i(int x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+  return wave_reduce(x, [](int a, int b) { return a + b; });
+}
+// For the max, rows a row_bcast step does not write must see the identity
+// (-inf) rather than 0: it comes in through the DPP `old` operand.
+template <int kCtrl, int kRowMask>
+__device__ inline float dpp_src_max(float x) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, -INFINITY),
+                                                        __builtin_bit_cast(int, x), kCtrl,
+                                                        kRowMask, 0xF, false));
+}
+__device__ inline float wave_max(float x) {
+  x = fmaxf(x, dpp_src_max<0xB1, 0xF>(x));
+  x = fmaxf(x, dpp_src_max<0x4E, 0xF>(x));
+  x = fmaxf(x, dpp_src_max<0x141, 0xF>(x));
+  x = fmaxf(x, dpp_src_max<0x140, 0xF>(x));
+  x = fmaxf(x, dpp_src_max<0x142, 0xA>(x));
+  x = fmaxf(x, dpp_src_max<0x143, 0xC>(x));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
 // Bits of word `w` (blocks 32w .. 32w+31) that fall inside the STA box around
@@ -67,14 +94,15 @@ __device__ inline uint32_t sta_word(const Geo& g, int w, int t, int hb, int wb, 
   return bits;
 }
 
+// One wavefront per row of the workgroup's R rows (R * 64 threads).
 template <int D, int R, int J>
-__global__ void __launch_bounds__(256) mask_kernel(const Geo g, const float* __restrict__ qbar,
+__global__ void __launch_bounds__(R * 64) mask_kernel(const Geo g, const float* __restrict__ qbar,
                                                    const float* __restrict__ kbar, float scale,
                                                    float thr, int rt, int rh, int rw,
                                                    uint32_t* __restrict__ bits,
                                                    int32_t* __restrict__ count,
                                                    uint32_t* __restrict__ abits, int lds_stride) {
-  extern __shared__ float S[];   // [R][lds_stride] scaled scores
+  extern __shared__ float S[];   // [R][lds_stride] scores in the exp2 domain
   const int nb = g.nb;
   const int nw = (nb + 31) >> 5;
   const int64_t head = blockIdx.y;
@@ -98,7 +126,7 @@ __global__ void __launch_bounds__(256) mask_kernel(const Geo g, const float* __r
                                     : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const int ntiles = (nb + 15) >> 4;
-    for (int ct = wave; ct < ntiles; ct += kWaves) {
+    for (int ct = wave; ct < ntiles; ct += R) {
       const int col = ct * 16 + i16;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       f32x4 bv[D / 16];
@@ -126,7 +154,7 @@ __global__ void __launch_bounds__(256) mask_kernel(const Geo g, const float* __r
 
   // ---- 2./3. one wavefront per row: softmax numerators, CDF cut, STA ----
   const int pf = g.gh * g.gw;
-  for (int ri = wave; ri < R; ri += kWaves) {
+  for (int ri = wave; ri < R; ri += R) {
     const int row = r0 + ri;
     if (row >= nb) break;
     const float* srow = S + ri * lds_stride;
@@ -143,7 +171,7 @@ __global__ void __launch_bounds__(256) mask_kernel(const Geo g, const float* __r
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int c = lane + 64 * j;
-      e[j] = c < nb ? expf(e[j] - mx) : 0.f;
+      e[j] = c < nb ? __builtin_amdgcn_exp2f(e[j] - mx) : 0.f;
       part += e[j];
     }
     const float Z = wave_sum(part);
@@ -239,8 +267,10 @@ hipError_t launch_t(const Geo& g, const float* qbar, const float* kbar, float th
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const dim3 grid((g.nb + R - 1) / R, (unsigned)g.bh);
-  const float scale = 1.0f / sqrtf((float)D);
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, g, qbar, kbar, scale, thr, rt, rh, rw, bits,
+  // scores q.k / sqrt(d), carried in the exp2 domain (times log2 e), so the
+  // softmax numerators are exp2(s - max)
+  const float scale = 1.4426950408889634f / sqrtf((float)D);
+  hipLaunchKernelGGL(kern, grid, dim3(R * 64), lds, s, g, qbar, kbar, scale, thr, rt, rh, rw, bits,
                      cnt, abits, stride);
   return hipGetLastError();
 }
@@ -252,6 +282,7 @@ hipError_t launch_d(const Geo& g, const float* qbar, const float* kbar, float th
   if (nb <= 256) return launch_t<D, 16, 4>(g, qbar, kbar, thr, rt, rh, rw, bits, cnt, abits, s);
   if (nb <= 512) return launch_t<D, 16, 8>(g, qbar, kbar, thr, rt, rh, rw, bits, cnt, abits, s);
   if (nb <= 1024) return launch_t<D, 16, 16>(g, qbar, kbar, thr, rt, rh, rw, bits, cnt, abits, s);
+  if (nb <= 1280) return launch_t<D, 16, 20>(g, qbar, kbar, thr, rt, rh, rw, bits, cnt, abits, s);
   if (nb <= 1536) return launch_t<D, 16, 24>(g, qbar, kbar, thr, rt, rh, rw, bits, cnt, abits, s);
   if (nb <= 2048) return launch_t<D, 16, 32>(g, qbar, kbar, thr, rt, rh, rw, bits, cnt, abits, s);
   if (nb <= 2496) return launch_t<D, 16, 39>(g, qbar, kbar, thr, rt, rh, rw, bits, cnt, abits, s);
