@@ -86,7 +86,7 @@ def traffic_record(workload_is_default):
     try:
         text = open(path).read()
         src = b"".join(open(os.path.join(csrc, n), "rb").read()
-                       for n in ("attn_fwd.hip", "nabla_common.hpp"))
+                       for n in ("attn_fwd_vt.hip", "attn_common.hpp", "nabla_common.hpp"))
     except OSError:
         return None
     m = re.search(r"<!-- traffic-record: (\{.*?\}) -->", text)
@@ -300,8 +300,8 @@ def main():
             "thr": thr, "sta": list(sta),
         },
         "roofline": {
-            "kernel": ("nabla_attn_fwd_vt (attn_fwd_bf16_kernel, V^T operands)" if vt_path
-                       else "nabla_attn_fwd"),
+            "kernel": ("nabla_attn_fwd_vt (attn_fwd_vt_kernel)" if vt_path
+                       else "nabla_attn_fwd (attn_fwd_f32_kernel)"),
             "bound": "mfma",
             "achieved": round(attn_tflops, 2),
             "peak": BF16_PEAK_TFLOPS,
