@@ -72,3 +72,12 @@ def long_inputs():
 def test_long_sweep(long_inputs, thr, sta):
     cfg, (q, k, v) = long_inputs
     _run(cfg, q, k, v, thr=thr, sta=sta, label=f"long thr={thr} sta={sta}")
+
+
+def test_max_blocks():
+    """3840 blocks per head (64 frames at 720p), close to the library's 4096:
+    the longest kept lists and union schedules, and the widest mask row."""
+    cfg = synth.config("long", T=64, heads=2, thr=0.9)
+    log(f"max_blocks: generating inputs {cfg}")
+    q, k, v = synth.make_qkv(cfg, device="cuda")
+    _run(cfg, q, k, v, label="max_blocks")
