@@ -186,13 +186,17 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
 
   // ---- this lane's query row as the B operand of S^T = K Q^T ----
   const int qs = 32 * (wave & 1) + jl;   // slot in the query block
-  bool qvalid = false;
-  int64_t qoff = 0;
-  if (myq >= 0) {
+  // offset of this lane's query row in Q and O (recomputed for the epilogue
+  // rather than kept live through the loop)
+  auto query_row = [&](bool* valid) -> int64_t {
+    *valid = false;
+    if (myq < 0) return 0;
     const BlockCoord qc = block_coord(g, myq);
-    qvalid = (qs >> 3) < block_rows_valid(g, qc) && (qs & 7) < block_cols_valid(g, qc);
-    qoff = hoff + block_base(g, myq, qc) + (qs >> 3) * row_step + (qs & 7) * D;
-  }
+    *valid = (qs >> 3) < block_rows_valid(g, qc) && (qs & 7) < block_cols_valid(g, qc);
+    return hoff + block_base(g, myq, qc) + (qs >> 3) * row_step + (qs & 7) * D;
+  };
+  bool qvalid;
+  const int64_t qoff = query_row(&qvalid);
   bf16x8 qop[S::kSteps];
 #pragma unroll
   for (int s = 0; s < S::kSteps; ++s) {
@@ -213,13 +217,20 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
       *c = (lane & 7) ^ swz128(*r);
     }
   };
-  int kdma_full[S::kKOps];
+  // full-block offset of op i = kdma_lane[i & 1] + kdma_rows(i) * row_step:
+  // the op's 8-row group is uniform, its row-in-group and chunk depend on
+  // the lane and the op's parity only
+  int kdma_lane[2];
 #pragma unroll
-  for (int i = 0; i < S::kKOps; ++i) {
+  for (int par = 0; par < 2; ++par) {
     int r, c;
-    kdma_rc(i, &r, &c);
-    kdma_full[i] = (r >> 3) * row_step + (r & 7) * D + c * 8;
+    kdma_rc(par, &r, &c);
+    kdma_lane[par] = (r & 7) * D + c * 8;
   }
+  auto kdma_rows = [&](int i) {     // 8-row group of op i (wavefront-uniform)
+    return S::kWideK ? 2 * wave + (i >> 1) : 2 * wave + i;
+  };
+  auto kdma_full = [&](int i) { return kdma_rows(i) * row_step + kdma_lane[i & 1]; };
   // V^T op o: rows 8o + lane / 8, logical chunk (lane % 8) ^ g(row); g's
   // bit from row bit 3 equals o & 1, so even and odd ops differ
   int vdma[2];
@@ -260,14 +271,14 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
     if (rv == kP && cv == kP) {
 #pragma unroll
       for (int i = 0; i < S::kKOps; ++i)
-        dma16(base + kdma_full[i], dst + S::k_op_offset(wave * S::kKOps + i));
+        dma16(base + kdma_full(i), dst + S::k_op_offset(wave * S::kKOps + i));
     } else {                         // pad rows re-read row 0 of the block
 #pragma unroll
       for (int i = 0; i < S::kKOps; ++i) {
         int r, c;
         kdma_rc(i, &r, &c);
         const bool ok = (r >> 3) < rv && (r & 7) < cv;
-        dma16(base + (ok ? kdma_full[i] : c * 8), dst + S::k_op_offset(wave * S::kKOps + i));
+        dma16(base + (ok ? kdma_full(i) : c * 8), dst + S::k_op_offset(wave * S::kKOps + i));
       }
     }
   };
@@ -328,16 +339,16 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
   // One iteration's work: A(s+1) on K buffer kb (if DoA), B(s) on V^T buffer
   // vb (if DoB); sc holds S(s) (consumed), sn receives S(s+1).  Written as
   // slots -- one matrix instruction, its share of vector work, one operand
-  // read 6 slots ahead -- fenced so the compiler keeps that order: QK slots
+  // read 2 slots ahead -- fenced so the compiler keeps that order: QK slots
   // carry the exponentials of B(s), PV slots the row max of A(s+1).
-  auto body = [&](auto do_a, auto do_b, bool live_b, f32x16 (&sc)[2], f32x16 (&sn)[2],
-                  const char* kb, const char* vb) {
+  auto body = [&](auto do_a, auto do_b, bool run_a, bool live_b, f32x16 (&sc)[2],
+                  f32x16 (&sn)[2], const char* kb, const char* vb) {
     constexpr bool DoA = decltype(do_a)::value;
     constexpr bool DoB = decltype(do_b)::value;
     constexpr int NQ = DoA ? 2 * S::kSteps : 0;      // QK matrix instructions
     constexpr int NP = DoB ? 4 * S::kDTiles : 0;     // PV matrix instructions
     constexpr int NR = NQ + NP;                      // operand reads, K then V^T
-    constexpr int kAhead = NR < 6 ? NR : 6;
+    constexpr int kAhead = NR < 2 ? NR : 2;
     bf16x8 op[NR > 0 ? NR : 1];
     auto read = [&](int j) {
       if (j < NQ)
@@ -354,20 +365,27 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
       sn[0] = f32x16{};
       sn[1] = f32x16{};
       constexpr int kExpPerSlot = 32 / (NQ > 0 ? NQ : 1);   // score elements per QK slot
+      // two copies of the QK slots, with and without the matrix instructions
+      // (a wavefront that does not keep block s+1 skips them)
+      auto qk_slots = [&](auto with_mfma) {
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        const int kt = i / S::kSteps, st = i % S::kSteps;
-        sn[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], qop[st], sn[kt], 0, 0, 0);
-        if constexpr (DoB) {
+        for (int i = 0; i < NQ; ++i) {
+          const int kt = i / S::kSteps, st = i % S::kSteps;
+          if constexpr (decltype(with_mfma)::value)
+            sn[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], qop[st], sn[kt], 0, 0, 0);
+          if constexpr (DoB) {
 #pragma unroll
-          for (int e = 0; e < kExpPerSlot; e += 2) {
-            const int el = i * kExpPerSlot + e;      // element of sc: kt = el / 16, r = el % 16
-            exp_pair(sc, pop, el >> 4, el & 15, m_ref);
+            for (int e = 0; e < kExpPerSlot; e += 2) {
+              const int el = i * kExpPerSlot + e;    // element of sc: kt = el / 16, r = el % 16
+              exp_pair(sc, pop, el >> 4, el & 15, m_ref);
+            }
           }
+          if (i + kAhead < NR) read(i + kAhead);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        if (i + kAhead < NR) read(i + kAhead);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      };
+      if (run_a) qk_slots(std::true_type{});
+      else qk_slots(std::false_type{});
     } else if constexpr (DoB) {
 #pragma unroll
       for (int el = 0; el < 32; el += 2) exp_pair(sc, pop, el >> 4, el & 15, m_ref);
@@ -375,21 +393,28 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
     float mx = -INFINITY;
     if constexpr (DoB) {
       constexpr int kMaxPerSlot = 32 / NP;           // score elements of sn per PV slot
+      // two copies of the PV slots, with and without the matrix instructions
+      // (a wavefront that does not keep block s skips them)
+      auto pv_slots = [&](auto with_mfma) {
 #pragma unroll
-      for (int i = 0; i < NP; ++i) {
-        oacc[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[NQ + i], pop[(i & 3) >> 1][i & 1],
-                                                               oacc[i >> 2], 0, 0, 0);
-        if constexpr (DoA) {
+        for (int i = 0; i < NP; ++i) {
+          if constexpr (decltype(with_mfma)::value)
+            oacc[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                op[NQ + i], pop[(i & 3) >> 1][i & 1], oacc[i >> 2], 0, 0, 0);
+          if constexpr (DoA) {
 #pragma unroll
-          for (int e = 0; e < kMaxPerSlot; e += 2) {
-            const int el = i * kMaxPerSlot + e;
-            mx = fmaxf(mx, fmaxf(sn[el >> 4][el & 15], sn[el >> 4][(el & 15) + 1]));
+            for (int e = 0; e < kMaxPerSlot; e += 2) {
+              const int el = i * kMaxPerSlot + e;
+              mx = fmaxf(mx, fmaxf(sn[el >> 4][el & 15], sn[el >> 4][(el & 15) + 1]));
+            }
+            asm volatile("" ::"v"(mx));
           }
-          asm volatile("" ::"v"(mx));
+          if (NQ + i + kAhead < NR) read(NQ + i + kAhead);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        if (NQ + i + kAhead < NR) read(NQ + i + kAhead);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      };
+      if (live_b) pv_slots(std::true_type{});
+      else pv_slots(std::false_type{});
     } else if constexpr (DoA) {
 #pragma unroll
       for (int el = 0; el < 32; el += 2)
@@ -441,9 +466,12 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
     const char* kb = kbuf + ((s + 1) & 1) * S::kKBytes;
     const char* vb = vbuf + (s & 1) * S::kVBytes;
     using T = std::true_type;
-    // a step with work for either stage runs both (an unneeded S(s+1) is
-    // ignored, an unneeded B(s) adds zero weights): one register layout
-    if (do_a || do_b) body(T{}, T{}, do_b, sc, sn, kb, vb);
+    // a step with work for either stage runs one body: the matrix
+    // instructions of an unneeded stage are skipped, its vector work runs
+    // harmlessly (an unneeded max is ignored, unneeded exponentials get the
+    // reference +inf and are exactly 0), so all cases share one register
+    // layout
+    if (do_a || do_b) body(T{}, T{}, do_a, do_b, sc, sn, kb, vb);
     if (do_a) mx_cur = mx_next;
     e0 = e1;
     e1 = e2;
@@ -457,9 +485,11 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
   // ---- normalise and write this lane's query row ----
   const float l_tot = swap_sum(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (myq >= 0 && (qvalid || g.layout == 1)) {
-    OutT* orow = O + qoff;
-    const float sc = qvalid ? inv : 0.f;
+  bool ovalid;
+  const int64_t ooff = query_row(&ovalid);
+  if (myq >= 0 && (ovalid || g.layout == 1)) {
+    OutT* orow = O + ooff;
+    const float sc = ovalid ? inv : 0.f;
 #pragma unroll
     for (int dt = 0; dt < S::kDTiles; ++dt) {
 #pragma unroll
