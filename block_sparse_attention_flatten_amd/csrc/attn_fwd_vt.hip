@@ -82,12 +82,19 @@ typedef __attribute__((address_space(3))) void lds_void;
 // s_waitcnt vmcnt(0), leaving the other counters alone.
 __device__ inline void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Direct-to-LDS load of 16 bytes per lane: lane l of the wavefront writes
-// bytes [16 l, 16 l + 16) of the 1-KB LDS block at dst.
-__device__ inline void dma16(const __bf16* src, char* dst) {
+// Direct-to-LDS load of 16 bytes per lane through a buffer descriptor: lane
+// l reads bytes [soff + voff, +16) of the buffer and writes bytes
+// [16 l, 16 l + 16) of the 1-KB LDS block at dst.  The buffer form keeps the
+// tile address in scalar registers, and (unlike the global form) does not
+// make the compiler drain every outstanding LDS read at each LDS wait.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, char* dst) {
 #if defined(__HIP_DEVICE_COMPILE__)   // gfx950-only builtin: the host pass needs no body
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, soff, 0, 0);
 #endif
+}
+// Raw buffer descriptor over n bytes at p (gfx9 word 3: 32-bit data format).
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
 }
 
 __device__ inline float swap_max(float x) {   // max over lanes l and l ^ 32
@@ -262,31 +269,44 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
   };
   auto vread = [&](int dt, int i) { return vaddr[i] + dt * 32 * 128; };
 
+  // one descriptor per head and tensor: byte offsets within a head fit in 32
+  // bits (a head holds fewer than 2^31 elements)
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(K + hoff, 2u * (uint32_t)g.head_elems);
+  const __amdgpu_buffer_rsrc_t vrs =
+      buffer_rsrc(VT + head * nb * (int64_t)(kN * D), 2u * (uint32_t)(nb * kN * D));
+  uint32_t kdma_voff[2], vdma_voff[2];   // per-lane byte offsets
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    kdma_voff[par] = 2u * (uint32_t)kdma_lane[par];
+    vdma_voff[par] = 2u * (uint32_t)vdma[par];
+  }
   auto load_k = [&](int e, char* dst) {
     const int beta = e & 0xFFF;
     const BlockCoord bc = block_coord(g, beta);
     const int rv = block_rows_valid(g, bc);
     const int cv = block_cols_valid(g, bc);
-    const __bf16* base = K + hoff + block_base(g, beta, bc);
-    if (rv == kP && cv == kP) {
+    const uint32_t sb = 2u * (uint32_t)block_base(g, beta, bc);
+    if (rv == kP && cv == kP) {      // lane part in the vector offset, the rest scalar
 #pragma unroll
       for (int i = 0; i < S::kKOps; ++i)
-        dma16(base + kdma_full(i), dst + S::k_op_offset(wave * S::kKOps + i));
+        dma16(krs, kdma_voff[i & 1], sb + 2u * (uint32_t)(kdma_rows(i) * row_step),
+              dst + S::k_op_offset(wave * S::kKOps + i));
     } else {                         // pad rows re-read row 0 of the block
 #pragma unroll
       for (int i = 0; i < S::kKOps; ++i) {
         int r, c;
         kdma_rc(i, &r, &c);
         const bool ok = (r >> 3) < rv && (r & 7) < cv;
-        dma16(base + (ok ? kdma_full(i) : c * 8), dst + S::k_op_offset(wave * S::kKOps + i));
+        dma16(krs, 2u * (uint32_t)(ok ? kdma_full(i) : c * 8), sb,
+              dst + S::k_op_offset(wave * S::kKOps + i));
       }
     }
   };
   auto load_v = [&](int e, char* dst) {
-    const __bf16* base = VT + (head * nb + (e & 0xFFF)) * (int64_t)(kN * D);
+    const uint32_t sb = 2u * (uint32_t)((e & 0xFFF) * (kN * D));
 #pragma unroll
     for (int i = 0; i < S::kVOps; ++i)
-      dma16(base + vdma[i & 1] + i * 512, dst + (wave * S::kVOps + i) * 1024);
+      dma16(vrs, vdma_voff[i & 1], sb + 1024u * i, dst + (wave * S::kVOps + i) * 1024);
   };
 
   f32x16 oacc[S::kDTiles];
@@ -352,9 +372,9 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
     bf16x8 op[NR > 0 ? NR : 1];
     auto read = [&](int j) {
       if (j < NQ)
-        op[j] = *(const bf16x8*)(kb + kread(j / S::kSteps, j % S::kSteps));
+        op[j] = *(const bf16x8*)(kb + kread(j & 1, j >> 1));
       else
-        op[j] = *(const bf16x8*)(vb + vread((j - NQ) >> 2, (j - NQ) & 3));
+        op[j] = *(const bf16x8*)(vb + vread((j - NQ) % S::kDTiles, (j - NQ) / S::kDTiles));
     };
 #pragma unroll
     for (int j = 0; j < kAhead; ++j) read(j);
@@ -370,7 +390,7 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
       auto qk_slots = [&](auto with_mfma) {
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
-          const int kt = i / S::kSteps, st = i % S::kSteps;
+          const int kt = i & 1, st = i >> 1;     // the two score tiles alternate
           if constexpr (decltype(with_mfma)::value)
             sn[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], qop[st], sn[kt], 0, 0, 0);
           if constexpr (DoB) {
@@ -399,8 +419,8 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
           if constexpr (decltype(with_mfma)::value)
-            oacc[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                op[NQ + i], pop[(i & 3) >> 1][i & 1], oacc[i >> 2], 0, 0, 0);
+            oacc[i % S::kDTiles] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(   // d tiles rotate
+                op[NQ + i], pop[(i / S::kDTiles) >> 1][(i / S::kDTiles) & 1], oacc[i % S::kDTiles], 0, 0, 0);
           if constexpr (DoA) {
 #pragma unroll
             for (int e = 0; e < kMaxPerSlot; e += 2) {
