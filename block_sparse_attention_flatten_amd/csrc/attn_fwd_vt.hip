@@ -33,8 +33,8 @@
 // Softmax: S^T orientation, so a lane owns one query and 32 of its 64 keys;
 // the row max needs one lane <-> lane^32 exchange (v_permlane32_swap), the
 // row sum none until the end.  The running max moves only when a block's max
-// exceeds it by more than 2^8 in the exp2 domain (exact: O and the row sum
-// share the reference).  The row sum adds the bf16-ROUNDED weights, so O / l
+// exceeds it by more than 8 in the exp2 domain, a factor of 2^8 (exact: O
+// and the row sum share the reference).  The row sum adds the bf16-ROUNDED weights, so O / l
 // is an exact convex combination of the V rows the matrix cores saw.
 // Pad key rows of latent-edge blocks load row 0 of the block (a real key, so
 // the block max is unchanged) and get weight 0; pad queries are not written
@@ -359,7 +359,7 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
   // One iteration's work: A(s+1) on K buffer kb (if DoA), B(s) on V^T buffer
   // vb (if DoB); sc holds S(s) (consumed), sn receives S(s+1).  Written as
   // slots -- one matrix instruction, its share of vector work, one operand
-  // read 2 slots ahead -- fenced so the compiler keeps that order: QK slots
+  // read 3 slots ahead -- fenced so the compiler keeps that order: QK slots
   // carry the exponentials of B(s), PV slots the row max of A(s+1).
   auto body = [&](auto do_a, auto do_b, bool run_a, bool live_b, f32x16 (&sc)[2],
                   f32x16 (&sn)[2], const char* kb, const char* vb) {
@@ -368,7 +368,7 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
     constexpr int NQ = DoA ? 2 * S::kSteps : 0;      // QK matrix instructions
     constexpr int NP = DoB ? 4 * S::kDTiles : 0;     // PV matrix instructions
     constexpr int NR = NQ + NP;                      // operand reads, K then V^T
-    constexpr int kAhead = NR < 2 ? NR : 2;
+    constexpr int kAhead = NR < 3 ? NR : 3;
     bf16x8 op[NR > 0 ? NR : 1];
     auto read = [&](int j) {
       if (j < NQ)
