@@ -78,6 +78,11 @@ struct VtShape {
 __device__ inline int swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+
+// 16-byte LDS read at an absolute LDS address
+__device__ inline bf16x8 lds_read16(int addr) { return *(lds_bf16x8*)(uintptr_t)addr; }
 
 // s_waitcnt vmcnt(0), leaving the other counters alone.
 __device__ inline void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -250,6 +255,9 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
   // 4 bits with jl, so the tile index t only adds a constant; logical chunk
   // 2s + hl lands at physical 2(s ^ y) + z, so four lane addresses plus
   // immediate offsets cover every read.
+  // absolute LDS addresses (K buffer 0 / V^T buffer 0), so that each read
+  // is a register plus an immediate offset
+  const int lds0 = (int)(uintptr_t)(lds_char*)smem;
   int kaddr[4], vaddr[4];
   {
     const int gk = S::kWideK ? (jl & 7) : swz128(jl);
@@ -257,8 +265,8 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
     const int kbase = S::kWideK ? (jl >> 3) * S::kKGroupBytes + (jl & 7) * 256 : jl * 128;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      kaddr[q] = kbase + (((2 * q + hl) ^ gk) << 4);
-      vaddr[q] = jl * 128 + (((2 * q + hl) ^ gv) << 4);
+      kaddr[q] = lds0 + kbase + (((2 * q + hl) ^ gk) << 4);
+      vaddr[q] = lds0 + 2 * S::kKBytes + jl * 128 + (((2 * q + hl) ^ gv) << 4);
     }
   }
   auto kread = [&](int kt, int s) {  // K row 32kt + jl, logical chunk 2s + hl
@@ -362,7 +370,7 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
   // read 3 slots ahead -- fenced so the compiler keeps that order: QK slots
   // carry the exponentials of B(s), PV slots the row max of A(s+1).
   auto body = [&](auto do_a, auto do_b, bool run_a, bool live_b, f32x16 (&sc)[2],
-                  f32x16 (&sn)[2], const char* kb, const char* vb) {
+                  f32x16 (&sn)[2], int kb, int vb) {
     constexpr bool DoA = decltype(do_a)::value;
     constexpr bool DoB = decltype(do_b)::value;
     constexpr int NQ = DoA ? 2 * S::kSteps : 0;      // QK matrix instructions
@@ -372,9 +380,9 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
     bf16x8 op[NR > 0 ? NR : 1];
     auto read = [&](int j) {
       if (j < NQ)
-        op[j] = *(const bf16x8*)(kb + kread(j & 1, j >> 1));
+        op[j] = lds_read16(kb + kread(j & 1, j >> 1));
       else
-        op[j] = *(const bf16x8*)(vb + vread((j - NQ) % S::kDTiles, (j - NQ) / S::kDTiles));
+        op[j] = lds_read16(vb + vread((j - NQ) % S::kDTiles, (j - NQ) / S::kDTiles));
     };
 #pragma unroll
     for (int j = 0; j < kAhead; ++j) read(j);
@@ -382,8 +390,6 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
     // a block this wavefront does not keep enters with weight exactly 0
     const float m_ref = live_b ? m_run : INFINITY;
     if constexpr (DoA) {
-      sn[0] = f32x16{};
-      sn[1] = f32x16{};
       constexpr int kExpPerSlot = 32 / (NQ > 0 ? NQ : 1);   // score elements per QK slot
       // two copies of the QK slots, with and without the matrix instructions
       // (a wavefront that does not keep block s+1 skips them)
@@ -392,7 +398,8 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
         for (int i = 0; i < NQ; ++i) {
           const int kt = i & 1, st = i >> 1;     // the two score tiles alternate
           if constexpr (decltype(with_mfma)::value)
-            sn[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], qop[st], sn[kt], 0, 0, 0);
+            sn[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], qop[st], st == 0 ? f32x16{} : sn[kt],
+                                                             0, 0, 0);
           if constexpr (DoB) {
 #pragma unroll
             for (int e = 0; e < kExpPerSlot; e += 2) {
@@ -459,7 +466,7 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int s = 0; s < S::kSteps; ++s) ka[kt][s] = *(const bf16x8*)(kbuf + kread(kt, s));
+      for (int s = 0; s < S::kSteps; ++s) ka[kt][s] = lds_read16(kread(kt, s));
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -483,8 +490,8 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
     const bool do_b = (e0 >> mine_bit) & 1;
     const bool do_a = e1 >= 0 && ((e1 >> mine_bit) & 1);
     if (do_b) stage_b_pre(sc, e0);
-    const char* kb = kbuf + ((s + 1) & 1) * S::kKBytes;
-    const char* vb = vbuf + (s & 1) * S::kVBytes;
+    const int kb = ((s + 1) & 1) * S::kKBytes;   // buffer offsets within the K / V^T areas
+    const int vb = (s & 1) * S::kVBytes;
     using T = std::true_type;
     // a step with work for either stage runs one body: the matrix
     // instructions of an unneeded stage are skipped, its vector work runs
