@@ -392,7 +392,9 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
     if constexpr (DoA) {
       constexpr int kExpPerSlot = 32 / (NQ > 0 ? NQ : 1);   // score elements per QK slot
       // two copies of the QK slots, with and without the matrix instructions
-      // (a wavefront that does not keep block s+1 skips them)
+      // (a wavefront that does not keep block s+1 skips them; sn then keeps
+      // an older finite score tile, whose max is ignored and whose weights
+      // are computed against the reference +inf, i.e. exactly 0)
       auto qk_slots = [&](auto with_mfma) {
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
