@@ -11,9 +11,10 @@
 // Wavefronts 0-1 own the first query block, 2-3 the second, 32 queries each.
 //
 // Prologue: the two kept lists are merged into an LDS list of 16-bit
-// entries (block index | in-first-list << 14 | in-second-list << 15) via LDS
-// bitmaps, so the main loop reads its schedule from LDS instead of chasing
-// list pointers.
+// entries (block index | latent-edge block << 12 | in-first-list << 14 |
+// in-second-list << 15) via LDS bitmaps, so the main loop reads its schedule
+// from LDS instead of chasing list pointers, and full blocks skip the edge
+// logic.
 //
 // Main loop, software-pipelined per wavefront.  Stage A(j) = S^T(j) = K(j) Q^T
 // on the matrix cores plus the row max of S(j); stage B(j) = online-softmax
@@ -80,6 +81,9 @@ __device__ inline int swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+
+// schedule entry flag: the block overhangs the latent edge (pad rows or columns)
+constexpr int kEdgeBit = 1 << 12;
 
 // 16-byte LDS read at an absolute LDS address
 __device__ inline bf16x8 lds_read16(int addr) { return *(lds_bf16x8*)(uintptr_t)addr; }
@@ -181,7 +185,10 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
       while (u) {
         const int bit = __builtin_ctz(u);
         u &= u - 1;
-        ul[pos++] = (uint16_t)((w << 5) | bit | (((a >> bit) & 1u) << 14) |
+        const int blk = (w << 5) | bit;
+        const BlockCoord c = block_coord(g, blk);
+        const bool edge = block_rows_valid(g, c) < kP || block_cols_valid(g, c) < kP;
+        ul[pos++] = (uint16_t)(blk | ((int)edge << 12) | (((a >> bit) & 1u) << 14) |
                                (((b >> bit) & 1u) << 15));
       }
     };
@@ -291,15 +298,15 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
   auto load_k = [&](int e, char* dst) {
     const int beta = e & 0xFFF;
     const BlockCoord bc = block_coord(g, beta);
-    const int rv = block_rows_valid(g, bc);
-    const int cv = block_cols_valid(g, bc);
     const uint32_t sb = 2u * (uint32_t)block_base(g, beta, bc);
-    if (rv == kP && cv == kP) {      // lane part in the vector offset, the rest scalar
+    if (!(e & kEdgeBit)) {           // lane part in the vector offset, the rest scalar
 #pragma unroll
       for (int i = 0; i < S::kKOps; ++i)
         dma16(krs, kdma_voff[i & 1], sb + 2u * (uint32_t)(kdma_rows(i) * row_step),
               dst + S::k_op_offset(wave * S::kKOps + i));
     } else {                         // pad rows re-read row 0 of the block
+      const int rv = block_rows_valid(g, bc);
+      const int cv = block_cols_valid(g, bc);
 #pragma unroll
       for (int i = 0; i < S::kKOps; ++i) {
         int r, c;
@@ -337,10 +344,10 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
       for (int t = 0; t < S::kDTiles; ++t) oacc[t] *= alpha;
       m_run = m_new;
     }
-    const BlockCoord bc = block_coord(g, e & 0xFFF);
-    const int rv = block_rows_valid(g, bc);
-    const int cv = block_cols_valid(g, bc);
-    if (rv < kP || cv < kP) {        // element r of sc[kt]: key row 4kt + r/4, column 4hl + r%4
+    if (e & kEdgeBit) {              // element r of sc[kt]: key row 4kt + r/4, column 4hl + r%4
+      const BlockCoord bc = block_coord(g, e & 0xFFF);
+      const int rv = block_rows_valid(g, bc);
+      const int cv = block_cols_valid(g, bc);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
