@@ -72,28 +72,43 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
 
 
+KERNEL_SOURCES = ("attn_fwd_vt.hip", "attn_common.hpp", "nabla_common.hpp")
+
+
+def kernel_source_digest():
+    """First 16 hex digits of the sha256 of the attention kernel's sources with
+    // comments and all white space removed (an edit to comments or layout does
+    not change it); None if a source is missing."""
+    import hashlib
+    import re
+    csrc = os.path.join(ROOT, "block_sparse_attention_flatten_amd", "csrc")
+    try:
+        text = "".join(open(os.path.join(csrc, n)).read() for n in KERNEL_SOURCES)
+    except OSError:
+        return None
+    code = re.sub(r"\s+", "", re.sub(r"//[^\n]*", "", text))
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
+
+
 def traffic_record(workload_is_default):
     """HBM bytes per launch of the attention kernel, from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the 720p workload.  Valid only
-    while the kernel source hashes to the value recorded there and the
-    workload is that default one; otherwise None."""
-    import hashlib
+    while the kernel's code (sources without comments) hashes to the value
+    recorded there and the workload is that default one; otherwise None."""
     import re
     if not workload_is_default:
         return None
     path = os.path.join(ROOT, "profiles", "attn_fwd_720p.md")
-    csrc = os.path.join(ROOT, "block_sparse_attention_flatten_amd", "csrc")
     try:
         text = open(path).read()
-        src = b"".join(open(os.path.join(csrc, n), "rb").read()
-                       for n in ("attn_fwd_vt.hip", "attn_common.hpp", "nabla_common.hpp"))
     except OSError:
         return None
     m = re.search(r"<!-- traffic-record: (\{.*?\}) -->", text)
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("source_sha256_16") != hashlib.sha256(src).hexdigest()[:16]:
+    digest = kernel_source_digest()
+    if digest is None or rec.get("code_sha256_16") != digest:
         return None
     return float(rec["traffic_bytes"])
 

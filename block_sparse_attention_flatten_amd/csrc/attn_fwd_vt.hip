@@ -22,24 +22,26 @@
 // B(s) interleaved -- the QK matrix instructions of block s+1 execute while
 // the exponentials of block s are computed, the PV instructions of block s
 // while the max of block s+1 is taken -- so the matrix cores and the vector
-// ALU work side by side inside one wavefront.
+// ALU work side by side inside one wavefront.  A wavefront whose query block
+// does not keep a block skips that stage's matrix instructions.
 //
-// Tiles move global -> LDS by direct-to-LDS loads (no register staging) into
-// two K and two V^T buffers.  Iteration s loads K(s+2) and V^T(s+1) into the
-// buffers that iteration s-1 finished with; one barrier per iteration
-// separates consumers and producers.  K rows are stored with the 16-byte
-// chunk index XOR-ed with (row & 7), V^T rows likewise, so the 8 rows that
-// one LDS read cycle serves fall in 8 distinct bank groups.
+// Tiles move global -> LDS by direct-to-LDS buffer loads (no register
+// staging) into two K and two V^T buffers.  Iteration s loads K(s+2) and
+// V^T(s+1) into the buffers that iteration s-1 finished with; one barrier per
+// iteration separates consumers and producers.  Tile rows are stored with
+// their 16-byte chunks permuted (layouts below) so that each LDS read cycle
+// hits distinct banks.
 //
 // Softmax: S^T orientation, so a lane owns one query and 32 of its 64 keys;
 // the row max needs one lane <-> lane^32 exchange (v_permlane32_swap), the
 // row sum none until the end.  The running max moves only when a block's max
 // exceeds it by more than 8 in the exp2 domain, a factor of 2^8 (exact: O
-// and the row sum share the reference).  The row sum adds the bf16-ROUNDED weights, so O / l
-// is an exact convex combination of the V rows the matrix cores saw.
-// Pad key rows of latent-edge blocks load row 0 of the block (a real key, so
-// the block max is unchanged) and get weight 0; pad queries are not written
-// in the natural layout and are written as zeros in the blocked layout.
+// and the row sum share the reference).  The row sum adds the bf16-ROUNDED
+// weights, so O / l is an exact convex combination of the V rows the matrix
+// cores saw.  Pad key rows of latent-edge blocks load row 0 of the block (a
+// real key, so the block max is unchanged) and get weight 0; pad queries are
+// not written in the natural layout and are written as zeros in the blocked
+// layout.
 #include <type_traits>
 
 #include "attn_common.hpp"
