@@ -32,13 +32,15 @@ __device__ inline void pair_of(const Geo& g, int p, int* a, int* b) {
 
 // Workgroup id -> (head, pair item).  Workgroups are dispatched in id order,
 // round-robin over the 8 XCDs (XCD = id % 8).  Each head's items are cut into
-// 8 contiguous chunks and XCD x takes chunk x of every head in turn: all XCDs
-// work on the same head at any time and each XCD's L2 sees one compact
-// spatial region whose kept lists overlap.  False for padding ids.
+// 8 contiguous chunks and XCD x takes chunk (x + h) % 8 of head h: all XCDs
+// work on the same head at any time, each XCD's L2 sees one compact spatial
+// region whose kept lists overlap, and the rotation spreads chunks that are
+// systematically heavier (say, frames with more kept keys) over all XCDs.
+// False for padding ids.
 __device__ inline bool xcd_item(int bid, int items, int chunk, int64_t* head, int* item) {
   const int x = bid & 7, i = bid >> 3;
   const int h = i / chunk;
-  const int it = x * chunk + (i - h * chunk);
+  const int it = ((x + h) & 7) * chunk + (i - h * chunk);
   *head = h;
   *item = it;
   return it < items;
