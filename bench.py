@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--sta", type=str, default=None, help="e.g. 3,3,3 or 0,0,0")
     ap.add_argument("--heads", type=int, default=None, help="override the head count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense reference (the same kernel with every block kept)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -345,6 +347,28 @@ def main():
                                       int(per_row.max())],
         "gpu": torch.cuda.get_device_name(0),
     }
+    if not args.no_dense:
+        # dense reference: the same attention kernel with every block kept (the
+        # mask of thr = 1 without STA), i.e. full attention over all valid keys
+        rp_full = (torch.arange(nb + 1, dtype=torch.int32, device=dev) * nb).expand(B * h, nb + 1)
+        rp_full = rp_full.contiguous()
+        ci_full = torch.arange(nb, dtype=torch.int32, device=dev).repeat(B * h, nb).contiguous()
+
+        def dense():
+            if vt_path:
+                nabla.nabla_attn_fwd_vt(g, q, k, vt, rp_full, ci_full, scale, o, stream)
+            else:
+                nabla.nabla_attn_fwd(g, q, k, v, rp_full, ci_full, scale, o, stream)
+        dense_ms = time_call(dense, reps=3)
+        dense_flops = B * h * nb * nb * 4 * 64 * 64 * d
+        result["dense_reference"] = {
+            "what": "same kernel, every block kept (thr = 1, no STA): full attention",
+            "ms": round(dense_ms, 3),
+            "tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 1),
+            "speedup_sparse_vs_dense": round(dense_ms / attn_avg, 3),
+        }
+        log(f"dense reference: {dense_ms:.2f} ms ({result['dense_reference']['tflops']} TFLOP/s)")
+        del rp_full, ci_full
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, thr, sta, args.cpu_seconds)
