@@ -33,6 +33,8 @@ design notes):
   * STA: a window of (wt, wh, ww) blocks centred on the query block in
     (frame, block-row, block-column) coordinates, clipped at the borders.
   * attention: pad keys never receive weight; pad queries produce zeros.
+  * gradients: the kept-block mask is held fixed (it is a threshold, so it
+    has no useful derivative); pad slots receive zero gradient.
 
 Pins: every function here is checked by tests against values the pages fix,
 closed forms, library routines or brute force (tests/test_oracle_pins.py).
@@ -49,7 +51,8 @@ import numpy as np
 __all__ = [
     "Geometry", "flatten_positions", "flatten", "unflatten", "valid_tokens",
     "pool", "reduced_map", "cdf_keep_row", "cdf_keep", "sta_mask", "nabla_mask",
-    "to_csr", "block_sparse_attention", "band_rows", "nabla_forward",
+    "to_csr", "block_sparse_attention", "block_sparse_attention_backward", "band_rows",
+    "nabla_forward",
 ]
 
 
@@ -259,6 +262,63 @@ def block_sparse_attention(qb: np.ndarray, kb: np.ndarray, vb: np.ndarray,
         w = w / w.sum(axis=1, keepdims=True)
         out[a][valid[a]] = w @ vals
     return out
+
+
+# ---------------------------------------------------------------------------
+# gradients of step 7 with the mask held fixed (training with NABLA:
+# [GZ] core contributions, acceleration of pre-training / fine-tuning, and
+# experimental results 2, pre-training of a 2B DiT; [LS] sec. 3)
+# ---------------------------------------------------------------------------
+def block_sparse_attention_backward(qb: np.ndarray, kb: np.ndarray, vb: np.ndarray,
+                                    m: np.ndarray, valid: np.ndarray, dob: np.ndarray,
+                                    scale: Optional[float] = None):
+    """One head: gradients of L = sum(dob * o) for o = block_sparse_attention(...).
+
+    The kept-block mask is a piecewise-constant function of q and k (a
+    threshold on pooled scores), so it is held fixed: only the exact
+    attention over the kept blocks is differentiated.  Plain definition:
+    p = softmax(s), s = q k^T * scale over the valid keys of the kept blocks,
+    o = p v; dv = p^T do, dp = do v^T, ds = p (dp - rowsum(do * o)),
+    dq = ds k * scale, dk = ds^T q * scale.
+
+    qb, kb, vb, dob: [nb, N, d]; m: [nb, nb] bool; valid: [nb, N] bool.
+    Returns dq, dk, dv [nb, N, d] float64 (zero at pad slots) and lse [nb, N],
+    the natural-log log-sum-exp of each valid query's scores (-inf for pad
+    queries and for rows without keys).
+    """
+    qb = np.asarray(qb, dtype=np.float64)
+    kb = np.asarray(kb, dtype=np.float64)
+    vb = np.asarray(vb, dtype=np.float64)
+    dob = np.asarray(dob, dtype=np.float64)
+    nb, N, d = qb.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dq = np.zeros((nb, N, d))
+    dk = np.zeros((nb, N, d))
+    dv = np.zeros((nb, N, d))
+    lse = np.full((nb, N), -np.inf)
+    slot = np.arange(N)
+    for a in range(nb):
+        cols = np.flatnonzero(m[a])
+        kblk = np.repeat(cols, N)[valid[cols].ravel()]          # key token -> block
+        kslot = np.tile(slot, len(cols))[valid[cols].ravel()]   # key token -> slot
+        if kblk.size == 0:
+            continue
+        keys, vals = kb[kblk, kslot], vb[kblk, kslot]         # [n_keys, d]
+        qi = np.flatnonzero(valid[a])
+        q, do = qb[a, qi], dob[a, qi]                          # [n_q, d]
+        s = (q @ keys.T) * scale
+        mx = s.max(axis=1, keepdims=True)
+        w = np.exp(s - mx)
+        z = w.sum(axis=1, keepdims=True)
+        p = w / z
+        lse[a, qi] = (mx + np.log(z))[:, 0]
+        o = p @ vals
+        dp = do @ vals.T
+        ds = p * (dp - (do * o).sum(axis=1, keepdims=True))
+        dq[a, qi] = (ds @ keys) * scale
+        np.add.at(dk, (kblk, kslot), (ds.T @ q) * scale)
+        np.add.at(dv, (kblk, kslot), p.T @ do)
+    return dq, dk, dv, lse
 
 
 # ---------------------------------------------------------------------------

@@ -294,6 +294,87 @@ def pin_attention_special_values(O):
         assert np.abs(ob[a] - want).max() < 1e-13
 
 
+# ------------------------------------------------------------------ gradients
+def _bwd_case(O, rng, T, H, W, d, density):
+    """Blocked random inputs (pad slots random too) and a random mask with the
+    diagonal kept, so every valid query sees at least one valid key."""
+    g = O.Geometry(T, H, W, 8)
+    valid = O.valid_tokens(g)
+    qb, kb, vb, dob = (rng.standard_normal((g.nb, 64, d)) for _ in range(4))
+    m = rng.random((g.nb, g.nb)) < density
+    m[np.arange(g.nb), np.arange(g.nb)] = True
+    return g, valid, qb, kb, vb, dob, m
+
+
+def pin_backward_finite_differences(O):
+    """Analytic gradients = central differences of L = sum(do * o), o the
+    oracle's attention (itself pinned above); pad slots get zero gradient."""
+    rng = _rng(11)
+    g, valid, qb, kb, vb, dob, m = _bwd_case(O, rng, 1, 13, 16, 4, 0.5)
+    assert not valid.all() and not m.all()
+    dq, dk, dv, _ = O.block_sparse_attention_backward(qb, kb, vb, m, valid, dob)
+    grads = {"q": dq, "k": dk, "v": dv}
+
+    def loss(x):
+        return float((dob * O.block_sparse_attention(x["q"], x["k"], x["v"], m, valid)).sum())
+    h = 1e-6
+    vb_idx = np.argwhere(valid)
+    pad_idx = np.argwhere(~valid)
+    for name in ("q", "k", "v"):
+        picks = [tuple(vb_idx[i]) for i in rng.choice(len(vb_idx), 12, replace=False)]
+        picks += [tuple(pad_idx[i]) for i in rng.choice(len(pad_idx), 3, replace=False)]
+        for (b, t) in picks:
+            c = int(rng.integers(qb.shape[-1]))
+            x = {"q": qb.copy(), "k": kb.copy(), "v": vb.copy()}
+            x[name][b, t, c] += h
+            lp = loss(x)
+            x[name][b, t, c] -= 2 * h
+            lm = loss(x)
+            num = (lp - lm) / (2 * h)
+            ana = grads[name][b, t, c]
+            assert abs(num - ana) <= 1e-7 + 1e-6 * abs(ana), (name, b, t, c, num, ana)
+            if not valid[b, t]:
+                assert ana == 0.0
+
+
+def pin_backward_autograd(O):
+    """Gradients and log-sum-exp = torch autograd of float64
+    scaled_dot_product_attention with the kept blocks (and valid keys) as the
+    attention mask; the dense case is the all-kept mask."""
+    rng = _rng(12)
+    for (T, H, W, d, density) in [(2, 13, 19, 16, 0.4), (2, 16, 16, 8, 1.0)]:
+        g, valid, qb, kb, vb, dob, m = _bwd_case(O, rng, T, H, W, d, density)
+        dq, dk, dv, lse = O.block_sparse_attention_backward(qb, kb, vb, m, valid, dob)
+        vq = valid.reshape(-1)
+        allow = (np.kron(m, np.ones((64, 64), dtype=bool)) & vq[None, :])[vq]
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a))  # noqa: E731
+        q = t(qb.reshape(-1, d)[vq]).requires_grad_()
+        k = t(kb.reshape(-1, d)).requires_grad_()
+        v = t(vb.reshape(-1, d)).requires_grad_()
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q[None], k[None], v[None], attn_mask=t(allow)[None])[0]
+        (o * t(dob.reshape(-1, d)[vq])).sum().backward()
+        assert np.abs(dq.reshape(-1, d)[vq] - q.grad.numpy()).max() < 1e-10
+        assert np.abs(dk.reshape(-1, d) - k.grad.numpy()).max() < 1e-10
+        assert np.abs(dv.reshape(-1, d) - v.grad.numpy()).max() < 1e-10
+        assert np.all(dq.reshape(-1, d)[~vq] == 0)
+        s = (qb.reshape(-1, d)[vq] @ kb.reshape(-1, d).T) / math.sqrt(d)
+        want = scipy.special.logsumexp(np.where(allow, s, -np.inf), axis=1)
+        assert np.abs(lse.reshape(-1)[vq] - want).max() < 1e-12
+        assert np.all(np.isneginf(lse.reshape(-1)[~vq]))
+
+
+def pin_backward_invariants(O):
+    """Rows of p sum to 1, so the dv rows add up to the do rows; rows of ds sum
+    to 0, so the dk rows add up to 0 (per head)."""
+    rng = _rng(13)
+    g, valid, qb, kb, vb, dob, m = _bwd_case(O, rng, 2, 16, 24, 8, 0.3)
+    dq, dk, dv, _ = O.block_sparse_attention_backward(qb, kb, vb, m, valid, dob)
+    assert np.abs(dv.sum((0, 1)) - dob[valid].sum(0)).max() < 1e-10
+    assert np.abs(dk.sum((0, 1))).max() < 1e-10
+    assert np.abs(dq).max() > 1e-3 and np.abs(dk).max() > 1e-3
+
+
 # ----------------------------------------------------------------- band rows
 def pin_band_rows(O):
     p = np.array([[0.4, 0.2 + 3e-6, 0.15, 0.15, 0.1 - 3e-6],  # D_2 = thr + 3e-6: class a

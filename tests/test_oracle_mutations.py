@@ -154,6 +154,40 @@ def _band_first_kept(p, m_ad, thr, eps=1e-5):
     return a, b
 
 
+def _bwd_variant(no_rowsum=False, dk_scale=True, dp_keys=False):
+    def f(qb, kb, vb, m, valid, dob, scale=None):
+        qb, kb, vb, dob = (np.asarray(x, np.float64) for x in (qb, kb, vb, dob))
+        nb, N, d = qb.shape
+        sc = 1 / math.sqrt(d) if scale is None else scale
+        dq, dk, dv = (np.zeros((nb, N, d)) for _ in range(3))
+        lse = np.full((nb, N), -np.inf)
+        slot = np.arange(N)
+        for a in range(nb):
+            cols = np.flatnonzero(m[a])
+            kblk = np.repeat(cols, N)[valid[cols].ravel()]
+            kslot = np.tile(slot, len(cols))[valid[cols].ravel()]
+            keys, vals = kb[kblk, kslot], vb[kblk, kslot]
+            qi = np.flatnonzero(valid[a])
+            q, do = qb[a, qi], dob[a, qi]
+            s = q @ keys.T * sc
+            w = np.exp(s - s.max(1, keepdims=True))
+            p = w / w.sum(1, keepdims=True)
+            lse[a, qi] = scipy_lse(s)
+            o = p @ vals
+            dp = do @ (keys if dp_keys else vals).T
+            ds = p * dp if no_rowsum else p * (dp - (do * o).sum(1, keepdims=True))
+            dq[a, qi] = ds @ keys * sc
+            np.add.at(dk, (kblk, kslot), ds.T @ q * (sc if dk_scale else 1.0))
+            np.add.at(dv, (kblk, kslot), p.T @ do)
+        return dq, dk, dv, lse
+    return f
+
+
+def scipy_lse(s):
+    import scipy.special
+    return scipy.special.logsumexp(s, axis=1)
+
+
 MUTATIONS = {
     "flatten_col_major_in_patch": ("flatten_positions", _positions(_col_major)),
     "flatten_time_innermost": ("flatten_positions", _positions(_time_inner)),
@@ -173,6 +207,9 @@ MUTATIONS = {
     "attn_softmax_wrong_axis": ("block_sparse_attention", _attn_variant(axis=0)),
     "csr_descending": ("to_csr", _csr_desc),
     "band_uses_top_block": ("band_rows", _band_first_kept),
+    "bwd_without_rowsum_term": ("block_sparse_attention_backward", _bwd_variant(no_rowsum=True)),
+    "bwd_dk_unscaled": ("block_sparse_attention_backward", _bwd_variant(dk_scale=False)),
+    "bwd_dp_uses_keys": ("block_sparse_attention_backward", _bwd_variant(dp_keys=True)),
 }
 
 
