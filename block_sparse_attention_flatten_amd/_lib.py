@@ -49,6 +49,14 @@ SIGNATURES = {
     "nabla_attn_fwd": ([_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
     "nabla_transpose_v": ([_G, _P, _P, _P], ctypes.c_int),
     "nabla_attn_fwd_vt": ([_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
+    "nabla_attn_fwd_lse": ([_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P], ctypes.c_int),
+    "nabla_attn_fwd_vt_lse": ([_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P],
+                              ctypes.c_int),
+    "nabla_mask_transpose": ([_G, _P, _P, _P, _P], ctypes.c_int),
+    "nabla_attn_bwd_dq": ([_G, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P],
+                          ctypes.c_int),
+    "nabla_attn_bwd_dkdv": ([_G, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P],
+                            ctypes.c_int),
     "nabla_forward_workspace_size": ([_G, _SZP, _SZP], ctypes.c_int),
     "nabla_forward": ([_G, _P, _P, _P, ctypes.c_float, _I32P, ctypes.c_float, _P, _P,
                        ctypes.c_size_t, _P], ctypes.c_int),

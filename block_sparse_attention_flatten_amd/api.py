@@ -25,7 +25,8 @@ __all__ = [
     "NablaError", "Geometry", "nabla_num_blocks", "nabla_flatten", "nabla_unflatten",
     "nabla_pool", "nabla_mask", "nabla_compact", "nabla_attn_fwd", "nabla_transpose_v",
     "nabla_attn_fwd_vt", "nabla_forward_workspace_size", "nabla_forward", "nabla_status_string",
-    "forward", "vt_shape",
+    "nabla_attn_fwd_lse", "nabla_attn_fwd_vt_lse", "nabla_mask_transpose", "nabla_attn_bwd_dq",
+    "nabla_attn_bwd_dkdv", "forward", "backward", "vt_shape", "lse_shape",
     "LAYOUT_THW", "LAYOUT_BLOCKED",
 ]
 
@@ -224,6 +225,74 @@ def nabla_attn_fwd_vt(g: Geometry, q, k, vt, row_ptr, col_idx, scale: float, o,
         _ptr(o, "o", shp, g.odtype), _stream(stream)), "nabla_attn_fwd_vt")
 
 
+def lse_shape(g: Geometry) -> Tuple[int, ...]:
+    """Shape of the per-query float32 lse / delta arrays [B, heads, nb, 64]."""
+    return (g.batch, g.heads, g.nb, 64)
+
+
+def nabla_attn_fwd_lse(g: Geometry, q, k, v, row_ptr, col_idx, scale: float, o, lse,
+                       stream=None) -> None:
+    shp = g.tensor_shape()
+    bh = g.batch * g.heads
+    _check(_lib.load().nabla_attn_fwd_lse(
+        ctypes.byref(g.c()), _ptr(q, "q", shp, g.dtype), _ptr(k, "k", shp, g.dtype),
+        _ptr(v, "v", shp, g.dtype), _ptr(row_ptr, "row_ptr", (bh, g.nb + 1), torch.int32),
+        _ptr(col_idx, "col_idx", (bh, g.nb * g.nb), torch.int32), float(scale),
+        _ptr(o, "o", shp, g.odtype), _ptr(lse, "lse", lse_shape(g), torch.float32),
+        _stream(stream)), "nabla_attn_fwd_lse")
+
+
+def nabla_attn_fwd_vt_lse(g: Geometry, q, k, vt, row_ptr, col_idx, scale: float, o, lse,
+                          stream=None) -> None:
+    shp = g.tensor_shape()
+    bh = g.batch * g.heads
+    _check(_lib.load().nabla_attn_fwd_vt_lse(
+        ctypes.byref(g.c()), _ptr(q, "q", shp, g.dtype), _ptr(k, "k", shp, g.dtype),
+        _ptr(vt, "vt", vt_shape(g), g.dtype),
+        _ptr(row_ptr, "row_ptr", (bh, g.nb + 1), torch.int32),
+        _ptr(col_idx, "col_idx", (bh, g.nb * g.nb), torch.int32), float(scale),
+        _ptr(o, "o", shp, g.odtype), _ptr(lse, "lse", lse_shape(g), torch.float32),
+        _stream(stream)), "nabla_attn_fwd_vt_lse")
+
+
+def nabla_mask_transpose(g: Geometry, mask_bits, mask_bits_t, row_count_t, stream=None) -> None:
+    bshape = (g.batch, g.heads, g.nb, g.nw)
+    _check(_lib.load().nabla_mask_transpose(
+        ctypes.byref(g.c()), _ptr(mask_bits, "mask_bits", bshape, torch.int32),
+        _ptr(mask_bits_t, "mask_bits_t", bshape, torch.int32),
+        _ptr(row_count_t, "row_count_t", (g.batch, g.heads, g.nb), torch.int32),
+        _stream(stream)), "nabla_mask_transpose")
+
+
+def nabla_attn_bwd_dq(g: Geometry, q, k, v, o, dout, lse, row_ptr, col_idx, scale: float, dq,
+                      delta, stream=None) -> None:
+    shp = g.tensor_shape()
+    bh = g.batch * g.heads
+    _check(_lib.load().nabla_attn_bwd_dq(
+        ctypes.byref(g.c()), _ptr(q, "q", shp, g.dtype), _ptr(k, "k", shp, g.dtype),
+        _ptr(v, "v", shp, g.dtype), _ptr(o, "o", shp, g.dtype), _ptr(dout, "dout", shp, g.dtype),
+        _ptr(lse, "lse", lse_shape(g), torch.float32),
+        _ptr(row_ptr, "row_ptr", (bh, g.nb + 1), torch.int32),
+        _ptr(col_idx, "col_idx", (bh, g.nb * g.nb), torch.int32), float(scale),
+        _ptr(dq, "dq", shp, g.dtype), _ptr(delta, "delta", lse_shape(g), torch.float32),
+        _stream(stream)), "nabla_attn_bwd_dq")
+
+
+def nabla_attn_bwd_dkdv(g: Geometry, q, k, v, dout, lse, delta, col_ptr, row_idx, scale: float,
+                        dk, dv, stream=None) -> None:
+    shp = g.tensor_shape()
+    bh = g.batch * g.heads
+    _check(_lib.load().nabla_attn_bwd_dkdv(
+        ctypes.byref(g.c()), _ptr(q, "q", shp, g.dtype), _ptr(k, "k", shp, g.dtype),
+        _ptr(v, "v", shp, g.dtype), _ptr(dout, "dout", shp, g.dtype),
+        _ptr(lse, "lse", lse_shape(g), torch.float32),
+        _ptr(delta, "delta", lse_shape(g), torch.float32),
+        _ptr(col_ptr, "col_ptr", (bh, g.nb + 1), torch.int32),
+        _ptr(row_idx, "row_idx", (bh, g.nb * g.nb), torch.int32), float(scale),
+        _ptr(dk, "dk", shp, g.dtype), _ptr(dv, "dv", shp, g.dtype), _stream(stream)),
+        "nabla_attn_bwd_dkdv")
+
+
 def nabla_forward_workspace_size(g: Geometry) -> Tuple[int, Tuple[int, ...]]:
     size = ctypes.c_size_t(0)
     offs = (ctypes.c_size_t * _lib.WORKSPACE_PARTS)()
@@ -292,3 +361,34 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, thr: float,
         row_ptr=part(4, torch.int32, (bh, g.nb + 1)),
         col_idx=part(5, torch.int32, (bh, g.nb * g.nb)),
     )
+
+
+@dataclass
+class BackwardResult:
+    dq: torch.Tensor
+    dk: torch.Tensor
+    dv: torch.Tensor
+    delta: torch.Tensor
+    col_ptr: torch.Tensor
+    row_idx: torch.Tensor
+
+
+def backward(g: Geometry, q, k, v, o, lse, dout, mask_bits, row_ptr, col_idx,
+             scale: Optional[float] = None, stream=None) -> BackwardResult:
+    """Gradients of one call with its mask held fixed, from the forward's o,
+    lse (nabla_attn_fwd_lse / _vt_lse), mask bits and lists: transposed mask
+    -> key-major lists -> dQ (and D) -> dK, dV, all on one stream."""
+    scale = 1.0 / math.sqrt(g.head_dim) if scale is None else scale
+    dev = q.device
+    bh = g.batch * g.heads
+    bits_t = torch.empty_like(mask_bits)
+    cnt_t = torch.empty((g.batch, g.heads, g.nb), dtype=torch.int32, device=dev)
+    col_ptr = torch.empty((bh, g.nb + 1), dtype=torch.int32, device=dev)
+    row_idx = torch.empty((bh, g.nb * g.nb), dtype=torch.int32, device=dev)
+    nabla_mask_transpose(g, mask_bits, bits_t, cnt_t, stream)
+    nabla_compact(g, bits_t, cnt_t, col_ptr, row_idx, stream)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    delta = torch.empty(lse_shape(g), dtype=torch.float32, device=dev)
+    nabla_attn_bwd_dq(g, q, k, v, o, dout, lse, row_ptr, col_idx, scale, dq, delta, stream)
+    nabla_attn_bwd_dkdv(g, q, k, v, dout, lse, delta, col_ptr, row_idx, scale, dk, dv, stream)
+    return BackwardResult(dq, dk, dv, delta, col_ptr, row_idx)

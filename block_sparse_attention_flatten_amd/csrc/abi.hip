@@ -98,6 +98,40 @@ void workspace_parts(const Geo& g, bool bf16, size_t off[kWsParts], size_t* tota
 
 hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
+int attn_fwd_impl(const nabla_geom* geom, const void* q, const void* k, const void* v,
+                  const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
+                  float* lse, bool need_lse, void* stream) {
+  Geo g;
+  bool empty;
+  const int st = make_geo(geom, true, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (!scale_ok(scale)) return NABLA_E_SCALE;
+  if (empty) return NABLA_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || row_ptr == nullptr || col_idx == nullptr ||
+      o == nullptr || (need_lse && lse == nullptr))
+    return NABLA_E_NULL;
+  return hip_status(nabla::launch_attn_fwd(g, geom->dtype == NABLA_DTYPE_BF16,
+                                           geom->out_dtype == NABLA_DTYPE_BF16, q, k, v, row_ptr,
+                                           col_idx, scale, o, lse, as_stream(stream)));
+}
+
+int attn_fwd_vt_impl(const nabla_geom* geom, const void* q, const void* k, const void* vt,
+                     const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
+                     float* lse, bool need_lse, void* stream) {
+  Geo g;
+  bool empty;
+  const int st = make_geo(geom, true, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (geom->dtype != NABLA_DTYPE_BF16) return NABLA_E_DTYPE;
+  if (!scale_ok(scale)) return NABLA_E_SCALE;
+  if (empty) return NABLA_OK;
+  if (q == nullptr || k == nullptr || vt == nullptr || row_ptr == nullptr ||
+      col_idx == nullptr || o == nullptr || (need_lse && lse == nullptr))
+    return NABLA_E_NULL;
+  return hip_status(nabla::launch_attn_fwd_vt(g, geom->out_dtype == NABLA_DTYPE_BF16, q, k, vt,
+                                              row_ptr, col_idx, scale, o, lse, as_stream(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -203,18 +237,13 @@ int nabla_compact(const nabla_geom* geom, const uint32_t* mask_bits, const int32
 int nabla_attn_fwd(const nabla_geom* geom, const void* q, const void* k, const void* v,
                    const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
                    void* stream) {
-  Geo g;
-  bool empty;
-  const int st = make_geo(geom, true, &g, &empty);
-  if (st != NABLA_OK) return st;
-  if (!scale_ok(scale)) return NABLA_E_SCALE;
-  if (empty) return NABLA_OK;
-  if (q == nullptr || k == nullptr || v == nullptr || row_ptr == nullptr || col_idx == nullptr ||
-      o == nullptr)
-    return NABLA_E_NULL;
-  return hip_status(nabla::launch_attn_fwd(g, geom->dtype == NABLA_DTYPE_BF16,
-                                           geom->out_dtype == NABLA_DTYPE_BF16, q, k, v, row_ptr,
-                                           col_idx, scale, o, as_stream(stream)));
+  return attn_fwd_impl(geom, q, k, v, row_ptr, col_idx, scale, o, nullptr, false, stream);
+}
+
+int nabla_attn_fwd_lse(const nabla_geom* geom, const void* q, const void* k, const void* v,
+                       const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
+                       float* lse, void* stream) {
+  return attn_fwd_impl(geom, q, k, v, row_ptr, col_idx, scale, o, lse, true, stream);
 }
 
 int nabla_transpose_v(const nabla_geom* geom, const void* v, void* vt, void* stream) {
@@ -231,18 +260,66 @@ int nabla_transpose_v(const nabla_geom* geom, const void* v, void* vt, void* str
 int nabla_attn_fwd_vt(const nabla_geom* geom, const void* q, const void* k, const void* vt,
                       const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
                       void* stream) {
+  return attn_fwd_vt_impl(geom, q, k, vt, row_ptr, col_idx, scale, o, nullptr, false, stream);
+}
+
+int nabla_attn_fwd_vt_lse(const nabla_geom* geom, const void* q, const void* k, const void* vt,
+                          const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
+                          float* lse, void* stream) {
+  return attn_fwd_vt_impl(geom, q, k, vt, row_ptr, col_idx, scale, o, lse, true, stream);
+}
+
+int nabla_mask_transpose(const nabla_geom* geom, const uint32_t* mask_bits, uint32_t* mask_bits_t,
+                         int32_t* row_count_t, void* stream) {
+  Geo g;
+  bool empty;
+  const int st = make_geo(geom, false, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (empty) return NABLA_OK;
+  if (mask_bits == nullptr || mask_bits_t == nullptr || row_count_t == nullptr)
+    return NABLA_E_NULL;
+  return hip_status(
+      nabla::launch_mask_transpose(g, mask_bits, mask_bits_t, row_count_t, as_stream(stream)));
+}
+
+int nabla_attn_bwd_dq(const nabla_geom* geom, const void* q, const void* k, const void* v,
+                      const void* o, const void* dout, const float* lse, const int32_t* row_ptr,
+                      const int32_t* col_idx, float scale, void* dq, float* delta,
+                      void* stream) {
   Geo g;
   bool empty;
   const int st = make_geo(geom, true, &g, &empty);
   if (st != NABLA_OK) return st;
-  if (geom->dtype != NABLA_DTYPE_BF16) return NABLA_E_DTYPE;
+  if (geom->out_dtype != geom->dtype) return NABLA_E_DTYPE;
   if (!scale_ok(scale)) return NABLA_E_SCALE;
   if (empty) return NABLA_OK;
-  if (q == nullptr || k == nullptr || vt == nullptr || row_ptr == nullptr ||
-      col_idx == nullptr || o == nullptr)
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr ||
+      lse == nullptr || row_ptr == nullptr || col_idx == nullptr || dq == nullptr ||
+      delta == nullptr)
     return NABLA_E_NULL;
-  return hip_status(nabla::launch_attn_fwd_vt(g, geom->out_dtype == NABLA_DTYPE_BF16, q, k, vt,
-                                              row_ptr, col_idx, scale, o, as_stream(stream)));
+  return hip_status(nabla::launch_attn_bwd_dq(g, geom->dtype == NABLA_DTYPE_BF16, q, k, v, o,
+                                              dout, lse, row_ptr, col_idx, scale, dq, delta,
+                                              as_stream(stream)));
+}
+
+int nabla_attn_bwd_dkdv(const nabla_geom* geom, const void* q, const void* k, const void* v,
+                        const void* dout, const float* lse, const float* delta,
+                        const int32_t* col_ptr, const int32_t* row_idx, float scale, void* dk,
+                        void* dv, void* stream) {
+  Geo g;
+  bool empty;
+  const int st = make_geo(geom, true, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (geom->out_dtype != geom->dtype) return NABLA_E_DTYPE;
+  if (!scale_ok(scale)) return NABLA_E_SCALE;
+  if (empty) return NABLA_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || dout == nullptr || lse == nullptr ||
+      delta == nullptr || col_ptr == nullptr || row_idx == nullptr || dk == nullptr ||
+      dv == nullptr)
+    return NABLA_E_NULL;
+  return hip_status(nabla::launch_attn_bwd_dkdv(g, geom->dtype == NABLA_DTYPE_BF16, q, k, v, dout,
+                                                lse, delta, col_ptr, row_idx, scale, dk, dv,
+                                                as_stream(stream)));
 }
 
 int nabla_forward_workspace_size(const nabla_geom* geom, size_t* bytes, size_t* offsets) {
@@ -292,9 +369,10 @@ int nabla_forward(const nabla_geom* geom, const void* q, const void* k, const vo
   if (bf16) {
     void* vt = ws + off[6];
     if (e == hipSuccess) e = nabla::launch_transpose_v(g, v, vt, s);
-    if (e == hipSuccess) e = nabla::launch_attn_fwd_vt(g, out_bf16, q, k, vt, rp, ci, scale, o, s);
+    if (e == hipSuccess)
+      e = nabla::launch_attn_fwd_vt(g, out_bf16, q, k, vt, rp, ci, scale, o, nullptr, s);
   } else if (e == hipSuccess) {
-    e = nabla::launch_attn_fwd(g, false, false, q, k, v, rp, ci, scale, o, s);
+    e = nabla::launch_attn_fwd(g, false, false, q, k, v, rp, ci, scale, o, nullptr, s);
   }
   return hip_status(e);
 }

@@ -1,0 +1,651 @@
+// Gradients of the block-sparse attention with the kept-block mask held fixed
+// (training with NABLA: "NABLA: Neighborhood Adaptive Block-Level Attention",
+// gist.science, core contributions -- pre-training / fine-tuning speed-up --
+// and experimental results 2, pre-training of a 2B DiT; lsdiaocha.cn article,
+// sec. 3).  The mask is a threshold on pooled scores, so only the exact
+// attention over the kept N x N blocks is differentiated:
+//   p = softmax(s), s = q k^T * scale;  dv = p^T do;  dp = do v^T;
+//   ds = p (dp - D), D = rowsum(do * o);  dq = ds k * scale;  dk = ds^T q * scale.
+// p is recomputed from the forward's log-sum-exp, so no N x N matrix is kept.
+//
+// Three calls:
+//   * mask transpose: key block c's list of the query blocks that keep it
+//     (bit r of transposed row c = bit c of row r), compacted by nabla_compact;
+//   * dQ: one workgroup per PAIR of query blocks walking the union of their
+//     kept lists (as the forward does); per kept block S^T = K Q^T and
+//     dP^T = V dO^T on the matrix cores, dS^T in registers, and
+//     dQ^T += K^T dS^T with K^T operands from transpose loads of the K tile.
+//     It also writes D = rowsum(dO * O) for the second call;
+//   * dK / dV: one workgroup per key block walking its query-block list.
+//     Wavefronts 0-1 accumulate dV^T += dO^T P, wavefronts 2-3 dK^T += Q^T dS
+//     (both recompute S = Q K^T; the dK side also dP = dO V^T), 32 keys each,
+//     so each lane owns one key and every accumulation stays in registers.
+// float32 inputs use plain per-thread kernels of the same structure.
+#include "attn_common.hpp"
+
+namespace nabla {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// transposed mask
+// ---------------------------------------------------------------------------
+// One wavefront per transposed row c (grid: nb x bh): 64 source rows per step,
+// the wanted bit of each gathered by a ballot.
+__global__ void __launch_bounds__(64)
+mask_transpose_kernel(const Geo g, const uint32_t* __restrict__ bits,
+                      uint32_t* __restrict__ bits_t, int32_t* __restrict__ count_t) {
+  const int nb = g.nb;
+  const int nw = (nb + 31) >> 5;
+  const int c = blockIdx.x;
+  const int64_t head = blockIdx.y;
+  const int lane = threadIdx.x;
+  const uint32_t* src = bits + head * (int64_t)nb * nw + (c >> 5);
+  uint32_t* dst = bits_t + (head * nb + c) * (int64_t)nw;
+  int cnt = 0;
+  for (int r0 = 0; r0 < nb; r0 += 64) {
+    const int r = r0 + lane;
+    const bool b = r < nb && ((src[(int64_t)r * nw] >> (c & 31)) & 1u);
+    const uint64_t m = __ballot(b);
+    const int w = r0 >> 5;
+    if (lane == 0) dst[w] = (uint32_t)m;
+    if (lane == 1 && w + 1 < nw) dst[w + 1] = (uint32_t)(m >> 32);
+    cnt += __popcll(m);
+  }
+  if (lane == 0) count_t[head * nb + c] = cnt;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernels
+// ---------------------------------------------------------------------------
+template <int D>
+struct BwdShape {
+  // LDS row stride (elements): a stride of 4 (mod 32) banks spreads the 16-byte
+  // row reads of 8 consecutive rows over all banks; the transpose loads of the
+  // same tile then see at most 2-way conflicts.
+  static constexpr int kStride = D + 8;
+  static constexpr int kThreads = 256;
+  static constexpr int kChunks = D / 8;           // 16-byte chunks per token row
+  static constexpr int kRowsPerPass = kThreads / kChunks;
+  static constexpr int kPasses = kN / kRowsPerPass;
+  static constexpr int kSteps = D / 16;           // k-steps over d
+  static constexpr int kDTiles = D / 32;          // 32-row tiles of a d x 32 accumulator
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Two 64 x d bf16 tiles (the same token block of two tensors) staged through
+// registers: fetch() loads the next block while the current one is in use,
+// put() writes the registers to LDS.  Pad rows of latent-edge blocks load row 0
+// of the block (finite data; their weights are forced to 0 by the caller).
+template <int D>
+struct TilePair {
+  using A = BwdShape<D>;
+  u32x4 r0[A::kPasses], r1[A::kPasses];
+  __device__ void fetch(const Geo& g, const __bf16* X0, const __bf16* X1, int64_t hoff,
+                        int row_step, int blk, int tid) {
+    const int chunk = tid % A::kChunks, row = tid / A::kChunks;
+    const BlockCoord bc = block_coord(g, blk);
+    const int rv = block_rows_valid(g, bc), cv = block_cols_valid(g, bc);
+    const int64_t base = hoff + block_base(g, blk, bc) + chunk * 8;
+#pragma unroll
+    for (int p = 0; p < A::kPasses; ++p) {
+      const int r = row + p * A::kRowsPerPass;
+      const bool ok = (r >> 3) < rv && (r & 7) < cv;
+      const int off = ok ? (r >> 3) * row_step + (r & 7) * D : 0;
+      r0[p] = *(const u32x4*)(X0 + base + off);
+      r1[p] = *(const u32x4*)(X1 + base + off);
+    }
+  }
+  __device__ void put(__bf16* T0, __bf16* T1, int tid) const {
+    const int chunk = tid % A::kChunks, row = tid / A::kChunks;
+#pragma unroll
+    for (int p = 0; p < A::kPasses; ++p) {
+      const int r = row + p * A::kRowsPerPass;
+      *(u32x4*)(T0 + r * A::kStride + chunk * 8) = r0[p];
+      *(u32x4*)(T1 + r * A::kStride + chunk * 8) = r1[p];
+    }
+  }
+};
+
+// A lane's token row as matrix-core operand chunks: chunk s holds elements
+// 16 s + 8 hl .. + 7 (zero when the row is not valid).
+template <int D>
+__device__ inline void row_operand(const __bf16* X, int64_t off, bool valid, int hl,
+                                   bf16x8 (&op)[D / 16]) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (valid) raw = *(const u32x4*)(X + off + 16 * s + 8 * hl);
+    op[s] = __builtin_bit_cast(bf16x8, raw);
+  }
+}
+
+// 32 x 32 product over d: acc[r] = sum_d T[row0 + jl][d] * op[d] with the
+// tile rows as the A operand (16-byte LDS row reads) and op as the B operand.
+template <int D>
+__device__ inline f32x16 rows_times(const __bf16* T, int row0, int jl, int hl,
+                                    const bf16x8 (&op)[D / 16]) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const bf16x8 a = *(const bf16x8*)(T + (row0 + jl) * BwdShape<D>::kStride + 16 * s + 8 * hl);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, op[s], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// acc[dt] += T^T[32 dt + lane % 32][rows] * B over the 32 tile rows
+// row0 .. row0 + 31, as two k-steps.  The A operand comes from the row-major
+// tile through transpose loads: in each 16-lane group, lane i receives element
+// i % 4 of the 4-element rows addressed by lanes 4e + i / 4, so the lane
+// supplying rows k0 + s / 4 and k0 + 8 + s / 4 (k0 = row0 + 16 h + 4 hl),
+// columns 32 dt + (lane & 16) + 4 (s % 4), yields exactly the k order of a
+// B operand built from a 32 x 32 accumulator (see to_bop).
+template <int D>
+__device__ inline void cols_times(const __bf16* T, int row0, int lane, int hl,
+                                  const bf16x8 (&bop)[2], f32x16 (&acc)[D / 32]) {
+  constexpr int St = BwdShape<D>::kStride;
+  const __bf16* src0 = T + ((lane & 15) >> 2) * St + (lane & 16) + 4 * (lane & 3);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const __bf16* src = src0 + (row0 + 16 * h + 4 * hl) * St + 32 * dt;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4*)(src));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4*)(src + 8 * St));
+      const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop[h], acc[dt], 0, 0, 0);
+    }
+  }
+}
+
+// Accumulator element r of a 32 x 32 tile sits in row 8 (r / 4) + 4 hl + r % 4
+// of this lane's column; as a B operand over those 32 rows, k-step h takes
+// elements 8 h .. 8 h + 7.
+__device__ inline void to_bop(const float (&x)[16], bf16x8 (&bop)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bop[h][e] = (__bf16)x[8 * h + e];
+}
+
+// store a lane's d-vector held as accumulator columns: element r of tile dt is
+// component 32 dt + 8 (r / 4) + 4 hl + r % 4
+template <int D>
+__device__ inline void store_row(__bf16* dst, const f32x16 (&acc)[D / 32], float mul, int hl) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq)
+      store4<__bf16>(dst + 32 * dt + 8 * gq + 4 * hl, acc[dt][4 * gq] * mul,
+                     acc[dt][4 * gq + 1] * mul, acc[dt][4 * gq + 2] * mul,
+                     acc[dt][4 * gq + 3] * mul);
+}
+
+// ---- dQ (and D) ----
+template <int D>
+__global__ void __launch_bounds__(256, 2)
+attn_bwd_dq_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                   const __bf16* __restrict__ V, const __bf16* __restrict__ O,
+                   const __bf16* __restrict__ dO, const float* __restrict__ lse,
+                   const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+                   float scale_log2, float scale, __bf16* __restrict__ dQ,
+                   float* __restrict__ delta) {
+  using A = BwdShape<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[kN * A::kStride];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[kN * A::kStride];
+
+  const int nb = g.nb;
+  const int items = pair_items(g);
+  int64_t head;
+  int item;
+  if (!xcd_item(blockIdx.x, items, (items + 7) >> 3, &head, &item)) return;
+  int qa, qpair;
+  pair_of(g, item, &qa, &qpair);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int grp = wave >> 1;
+  const int hl = lane >> 5;
+  const int jl = lane & 31;
+  const int myq = grp == 0 ? qa : qpair;
+  const int64_t hoff = head * (int64_t)g.head_elems;
+  const int row_step = block_row_step(g);
+
+  // this lane's query row: Q and dO as B operands, D = rowsum(dO * O)
+  const int qs = 32 * (wave & 1) + jl;
+  bool qvalid = false;
+  int64_t qoff = 0;
+  if (myq >= 0) {
+    const BlockCoord qc = block_coord(g, myq);
+    qvalid = (qs >> 3) < block_rows_valid(g, qc) && (qs & 7) < block_cols_valid(g, qc);
+    qoff = hoff + block_base(g, myq, qc) + (qs >> 3) * row_step + (qs & 7) * D;
+  }
+  bf16x8 qop[A::kSteps], doop[A::kSteps];
+  row_operand<D>(Q, qoff, qvalid, hl, qop);
+  row_operand<D>(dO, qoff, qvalid, hl, doop);
+  float dpart = 0.f;
+#pragma unroll
+  for (int s = 0; s < A::kSteps; ++s) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (qvalid) raw = *(const u32x4*)(O + qoff + 16 * s + 8 * hl);
+    const bf16x8 o8 = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dpart = fmaf((float)doop[s][e], (float)o8[e], dpart);
+  }
+  const float Dq = dpart + __shfl_xor(dpart, 32);
+  const int64_t slot = myq >= 0 ? (head * nb + myq) * kN + qs : 0;
+  if (myq >= 0 && hl == 0) delta[slot] = qvalid ? Dq : 0.f;
+  // p = exp2(s * scale_log2 - lse2); pad queries get lse2 = +inf, i.e. p = 0
+  float lse2 = INFINITY;
+  if (myq >= 0 && qvalid) {
+    const float l = lse[slot];
+    if (l > -INFINITY) lse2 = l * kLog2e;
+  }
+
+  f32x16 dqacc[A::kDTiles];
+#pragma unroll
+  for (int t = 0; t < A::kDTiles; ++t) dqacc[t] = f32x16{};
+
+  const int32_t* rp = row_ptr + head * (nb + 1);
+  const int32_t* cols = col_idx + head * (int64_t)nb * nb;
+  KeptList la = kept_list(rp, cols, nb, qa);
+  KeptList lb = kept_list(rp, cols, nb, qpair);
+  TilePair<D> pre;
+  int next = min(la.head, lb.head);
+  if (next != INT_MAX) pre.fetch(g, K, V, hoff, row_step, next, tid);
+  while (next != INT_MAX) {
+    const int beta = next;
+    const bool in_a = la.head == beta;
+    const bool in_b = lb.head == beta;
+    if (in_a) { ++la.i; la.settle(); }
+    if (in_b) { ++lb.i; lb.settle(); }
+    next = min(la.head, lb.head);
+    __syncthreads();                 // every wavefront is done with the previous tiles
+    pre.put(Ks, Vs, tid);
+    __syncthreads();
+    if (next != INT_MAX) pre.fetch(g, K, V, hoff, row_step, next, tid);
+    if (!(grp == 0 ? in_a : in_b)) continue;   // wavefront-uniform: not a kept block of ours
+
+    const BlockCoord bc = block_coord(g, beta);
+    const int rv = block_rows_valid(g, bc);
+    const int cv = block_cols_valid(g, bc);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      // S^T and dP^T for keys 32 kt .. 32 kt + 31 (rows) of this lane's query
+      const f32x16 sacc = rows_times<D>(Ks, 32 * kt, jl, hl, qop);
+      const f32x16 dpacc = rows_times<D>(Vs, 32 * kt, jl, hl, doop);
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const bool ok = (key >> 3) < rv && (key & 7) < cv;
+        const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2)) : 0.f;
+        ds[r] = p * (dpacc[r] - Dq);
+      }
+      bf16x8 bop[2];
+      to_bop(ds, bop);
+      cols_times<D>(Ks, 32 * kt, lane, hl, bop, dqacc);    // dQ^T += K^T dS^T
+    }
+  }
+
+  if (myq >= 0 && (qvalid || g.layout == 1))
+    store_row<D>(dQ + qoff, dqacc, qvalid ? scale : 0.f, hl);
+}
+
+// ---- dK and dV ----
+template <int D>
+__global__ void __launch_bounds__(256, 2)
+attn_bwd_dkdv_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                     const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                     const float* __restrict__ lse, const float* __restrict__ delta,
+                     const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx,
+                     float scale_log2, float scale, __bf16* __restrict__ dK,
+                     __bf16* __restrict__ dV) {
+  using A = BwdShape<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 Qs[kN * A::kStride];
+  __shared__ __attribute__((aligned(16))) __bf16 dOs[kN * A::kStride];
+  __shared__ __attribute__((aligned(16))) float Ls[kN];   // log2-domain lse (+inf: weight 0)
+  __shared__ __attribute__((aligned(16))) float Ds[kN];
+
+  const int nb = g.nb;
+  int64_t head;
+  int beta;
+  if (!xcd_item(blockIdx.x, nb, (nb + 7) >> 3, &head, &beta)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const bool dk_side = (wave >> 1) != 0;   // wavefronts 0-1: dV, 2-3: dK
+  const int hl = lane >> 5;
+  const int jl = lane & 31;
+  const int64_t hoff = head * (int64_t)g.head_elems;
+  const int row_step = block_row_step(g);
+
+  // this lane's key row: K (and V on the dK side) as B operands
+  const int ks = 32 * (wave & 1) + jl;
+  const BlockCoord kc = block_coord(g, beta);
+  const bool kvalid = (ks >> 3) < block_rows_valid(g, kc) && (ks & 7) < block_cols_valid(g, kc);
+  const int64_t koff = hoff + block_base(g, beta, kc) + (ks >> 3) * row_step + (ks & 7) * D;
+  bf16x8 kop[A::kSteps], vop[A::kSteps];
+  row_operand<D>(K, koff, kvalid, hl, kop);
+  row_operand<D>(V, koff, kvalid && dk_side, hl, vop);
+
+  f32x16 acc[A::kDTiles];
+#pragma unroll
+  for (int t = 0; t < A::kDTiles; ++t) acc[t] = f32x16{};
+
+  KeptList lq = kept_list(col_ptr + head * (nb + 1), row_idx + head * (int64_t)nb * nb, nb, beta);
+  TilePair<D> pre;
+  float lse_n = 0.f, del_n = 0.f;            // threads 0-63: the next block's lse and D
+  auto fetch = [&](int alpha) {
+    pre.fetch(g, Q, dO, hoff, row_step, alpha, tid);
+    if (tid < kN) {
+      const float l = lse[(head * nb + alpha) * kN + tid];
+      lse_n = l > -INFINITY ? l * kLog2e : INFINITY;
+      del_n = delta[(head * nb + alpha) * kN + tid];
+    }
+  };
+  if (lq.head != INT_MAX) fetch(lq.head);
+  while (lq.head != INT_MAX) {
+    ++lq.i;
+    lq.settle();
+    __syncthreads();
+    pre.put(Qs, dOs, tid);
+    if (tid < kN) {
+      Ls[tid] = lse_n;
+      Ds[tid] = del_n;
+    }
+    __syncthreads();
+    if (lq.head != INT_MAX) fetch(lq.head);
+
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      // S for queries 32 qt .. 32 qt + 31 (rows) and this lane's key (column)
+      const f32x16 sacc = rows_times<D>(Qs, 32 * qt, jl, hl, kop);
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 l4 = *(const f32x4*)(Ls + 32 * qt + 8 * i + 4 * hl);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)   // a pad key (zero row) keeps weight 0
+          x[4 * i + j] =
+              kvalid ? __builtin_amdgcn_exp2f(fmaf(sacc[4 * i + j], scale_log2, -l4[j])) : 0.f;
+      }
+      if (dk_side) {
+        const f32x16 dpacc = rows_times<D>(dOs, 32 * qt, jl, hl, vop);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 d4 = *(const f32x4*)(Ds + 32 * qt + 8 * i + 4 * hl);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[4 * i + j] *= dpacc[4 * i + j] - d4[j];
+        }
+        bf16x8 bop[2];
+        to_bop(x, bop);
+        cols_times<D>(Qs, 32 * qt, lane, hl, bop, acc);     // dK^T += Q^T dS
+      } else {
+        bf16x8 bop[2];
+        to_bop(x, bop);
+        cols_times<D>(dOs, 32 * qt, lane, hl, bop, acc);    // dV^T += dO^T P
+      }
+    }
+  }
+
+  if (kvalid || g.layout == 1) {
+    __bf16* dst = (dk_side ? dK : dV) + koff;
+    store_row<D>(dst, acc, kvalid ? (dk_side ? scale : 1.0f) : 0.f, hl);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 kernels: one thread per token, fp32 FMA
+// ---------------------------------------------------------------------------
+// dQ and D: one workgroup (64 threads) per query block, K and V tiles in LDS.
+template <int D>
+__global__ void __launch_bounds__(64)
+attn_bwd_dq_f32_kernel(const Geo g, const float* __restrict__ Q, const float* __restrict__ K,
+                       const float* __restrict__ V, const float* __restrict__ O,
+                       const float* __restrict__ dO, const float* __restrict__ lse,
+                       const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+                       float scale, float* __restrict__ dQ, float* __restrict__ delta) {
+  extern __shared__ __attribute__((aligned(16))) float smem_f[];
+  float* Kt = smem_f;
+  float* Vt = smem_f + kN * D;
+  const int nb = g.nb;
+  const int64_t head = blockIdx.x / nb;
+  const int qb = (int)(blockIdx.x - head * nb);
+  const int s = threadIdx.x;
+  const int64_t hoff = head * (int64_t)g.head_elems;
+  const int row_step = block_row_step(g);
+  const BlockCoord qc = block_coord(g, qb);
+  const bool qvalid = (s >> 3) < block_rows_valid(g, qc) && (s & 7) < block_cols_valid(g, qc);
+  const int64_t qoff = hoff + block_base(g, qb, qc) + (s >> 3) * row_step + (s & 7) * D;
+
+  float qv[D], dov[D], acc[D];
+  float Dq = 0.f;
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    qv[c] = qvalid ? Q[qoff + c] : 0.f;
+    dov[c] = qvalid ? dO[qoff + c] : 0.f;
+    Dq = fmaf(dov[c], qvalid ? O[qoff + c] : 0.f, Dq);
+    acc[c] = 0.f;
+  }
+  const int64_t slot = (head * nb + qb) * kN + s;
+  delta[slot] = Dq;
+  const float l = lse[slot];
+  const bool live = qvalid && l > -INFINITY;
+  const int32_t* rp = row_ptr + head * (nb + 1);
+  const int32_t* cols = col_idx + head * (int64_t)nb * nb;
+  const int begin = rp[qb];
+  int end = rp[qb + 1];
+  if (begin < 0 || end < begin || end > nb * nb) end = begin;   // malformed row: no keys
+  for (int idx = begin; idx < end; ++idx) {
+    const int beta = cols[idx];
+    if ((unsigned)beta >= (unsigned)nb) continue;               // uniform across the block
+    const BlockCoord bc = block_coord(g, beta);
+    const int rv = block_rows_valid(g, bc), cv = block_cols_valid(g, bc);
+    const int64_t base = hoff + block_base(g, beta, bc);
+    __syncthreads();
+    for (int i = threadIdx.x; i < kN * D / 4; i += 64) {
+      const int r = i / (D / 4), c4 = i % (D / 4);
+      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      if ((r >> 3) < rv && (r & 7) < cv) {
+        const int64_t off = base + (r >> 3) * row_step + (r & 7) * D + 4 * c4;
+        kv = *(const f32x4*)(K + off);
+        vv = *(const f32x4*)(V + off);
+      }
+      *(f32x4*)(Kt + r * D + 4 * c4) = kv;
+      *(f32x4*)(Vt + r * D + 4 * c4) = vv;
+    }
+    __syncthreads();
+    if (!live) continue;
+    for (int r = 0; r < kN; ++r) {
+      if (!((r >> 3) < rv && (r & 7) < cv)) continue;
+      float dot = 0.f, dp = 0.f;
+#pragma unroll
+      for (int c = 0; c < D; ++c) {
+        dot = fmaf(qv[c], Kt[r * D + c], dot);
+        dp = fmaf(dov[c], Vt[r * D + c], dp);
+      }
+      const float ds = expf(dot * scale - l) * (dp - Dq);
+#pragma unroll
+      for (int c = 0; c < D; ++c) acc[c] = fmaf(ds, Kt[r * D + c], acc[c]);
+    }
+  }
+  if (qvalid || g.layout == 1) {
+#pragma unroll
+    for (int c = 0; c < D; ++c) dQ[qoff + c] = qvalid ? acc[c] * scale : 0.f;
+  }
+}
+
+// dK (threads 64-127) and dV (threads 0-63): one workgroup per key block,
+// the Q and dO tiles of each listed query block in LDS.
+template <int D>
+__global__ void __launch_bounds__(128)
+attn_bwd_dkdv_f32_kernel(const Geo g, const float* __restrict__ Q, const float* __restrict__ K,
+                         const float* __restrict__ V, const float* __restrict__ dO,
+                         const float* __restrict__ lse, const float* __restrict__ delta,
+                         const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx,
+                         float scale, float* __restrict__ dK, float* __restrict__ dV) {
+  extern __shared__ __attribute__((aligned(16))) float smem_f[];
+  float* Qt = smem_f;
+  float* Gt = smem_f + kN * D;        // dO tile
+  float* Lt = smem_f + 2 * kN * D;    // lse of the tile's queries (-inf: pad)
+  float* Dt = Lt + kN;
+  const int nb = g.nb;
+  const int64_t head = blockIdx.x / nb;
+  const int kb = (int)(blockIdx.x - head * nb);
+  const int s = threadIdx.x & 63;
+  const bool dk_side = threadIdx.x >= 64;
+  const int64_t hoff = head * (int64_t)g.head_elems;
+  const int row_step = block_row_step(g);
+  const BlockCoord kc = block_coord(g, kb);
+  const bool kvalid = (s >> 3) < block_rows_valid(g, kc) && (s & 7) < block_cols_valid(g, kc);
+  const int64_t koff = hoff + block_base(g, kb, kc) + (s >> 3) * row_step + (s & 7) * D;
+
+  float kv[D], vv[D], acc[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    kv[c] = kvalid ? K[koff + c] : 0.f;
+    vv[c] = kvalid && dk_side ? V[koff + c] : 0.f;
+    acc[c] = 0.f;
+  }
+  const int32_t* cp = col_ptr + head * (nb + 1);
+  const int32_t* rows = row_idx + head * (int64_t)nb * nb;
+  const int begin = cp[kb];
+  int end = cp[kb + 1];
+  if (begin < 0 || end < begin || end > nb * nb) end = begin;
+  for (int idx = begin; idx < end; ++idx) {
+    const int alpha = rows[idx];
+    if ((unsigned)alpha >= (unsigned)nb) continue;
+    const BlockCoord ac = block_coord(g, alpha);
+    const int rv = block_rows_valid(g, ac), cv = block_cols_valid(g, ac);
+    const int64_t base = hoff + block_base(g, alpha, ac);
+    __syncthreads();
+    for (int i = threadIdx.x; i < kN * D / 4; i += 128) {
+      const int r = i / (D / 4), c4 = i % (D / 4);
+      f32x4 qq = {0.f, 0.f, 0.f, 0.f}, gg = {0.f, 0.f, 0.f, 0.f};
+      if ((r >> 3) < rv && (r & 7) < cv) {
+        const int64_t off = base + (r >> 3) * row_step + (r & 7) * D + 4 * c4;
+        qq = *(const f32x4*)(Q + off);
+        gg = *(const f32x4*)(dO + off);
+      }
+      *(f32x4*)(Qt + r * D + 4 * c4) = qq;
+      *(f32x4*)(Gt + r * D + 4 * c4) = gg;
+    }
+    if (threadIdx.x < kN) {
+      Lt[threadIdx.x] = lse[(head * nb + alpha) * kN + threadIdx.x];
+      Dt[threadIdx.x] = delta[(head * nb + alpha) * kN + threadIdx.x];
+    }
+    __syncthreads();
+    if (!kvalid) continue;
+    for (int r = 0; r < kN; ++r) {
+      if (!((r >> 3) < rv && (r & 7) < cv) || !(Lt[r] > -INFINITY)) continue;
+      float dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < D; ++c) dot = fmaf(Qt[r * D + c], kv[c], dot);
+      const float p = expf(dot * scale - Lt[r]);
+      if (dk_side) {
+        float dp = 0.f;
+#pragma unroll
+        for (int c = 0; c < D; ++c) dp = fmaf(Gt[r * D + c], vv[c], dp);
+        const float ds = p * (dp - Dt[r]);
+#pragma unroll
+        for (int c = 0; c < D; ++c) acc[c] = fmaf(ds, Qt[r * D + c], acc[c]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < D; ++c) acc[c] = fmaf(p, Gt[r * D + c], acc[c]);
+      }
+    }
+  }
+  if (kvalid || g.layout == 1) {
+    float* dst = (dk_side ? dK : dV) + koff;
+    const float mul = kvalid ? (dk_side ? scale : 1.0f) : 0.f;
+#pragma unroll
+    for (int c = 0; c < D; ++c) dst[c] = acc[c] * mul;
+  }
+}
+
+template <int D>
+hipError_t launch_dq_t(const Geo& g, bool bf16, const void* q, const void* k, const void* v,
+                       const void* o, const void* dout, const float* lse, const int32_t* row_ptr,
+                       const int32_t* col_idx, float scale, void* dq, float* delta,
+                       hipStream_t s) {
+  if (bf16) {
+    const int64_t chunk = (pair_items(g) + 7) / 8;
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3((unsigned)(8 * chunk * g.bh)), dim3(256), 0, s,
+                       g, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)o,
+                       (const __bf16*)dout, lse, row_ptr, col_idx, scale * kLog2e, scale,
+                       (__bf16*)dq, delta);
+    return hipGetLastError();
+  }
+  const size_t lds = 2 * kN * D * sizeof(float);
+  auto kern = attn_bwd_dq_f32_kernel<D>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(g.bh * g.nb)), dim3(64), lds, s, g, (const float*)q,
+                     (const float*)k, (const float*)v, (const float*)o, (const float*)dout, lse,
+                     row_ptr, col_idx, scale, (float*)dq, delta);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dkdv_t(const Geo& g, bool bf16, const void* q, const void* k, const void* v,
+                         const void* dout, const float* lse, const float* delta,
+                         const int32_t* col_ptr, const int32_t* row_idx, float scale, void* dk,
+                         void* dv, hipStream_t s) {
+  if (bf16) {
+    const int64_t chunk = (g.nb + 7) / 8;
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)(8 * chunk * g.bh)), dim3(256), 0,
+                       s, g, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
+                       (const __bf16*)dout, lse, delta, col_ptr, row_idx, scale * kLog2e, scale,
+                       (__bf16*)dk, (__bf16*)dv);
+    return hipGetLastError();
+  }
+  const size_t lds = (2 * kN * D + 2 * kN) * sizeof(float);
+  auto kern = attn_bwd_dkdv_f32_kernel<D>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(g.bh * g.nb)), dim3(128), lds, s, g, (const float*)q,
+                     (const float*)k, (const float*)v, (const float*)dout, lse, delta, col_ptr,
+                     row_idx, scale, (float*)dk, (float*)dv);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mask_transpose(const Geo& g, const uint32_t* bits, uint32_t* bits_t,
+                                 int32_t* count_t, hipStream_t s) {
+  hipLaunchKernelGGL(mask_transpose_kernel, dim3((unsigned)g.nb, (unsigned)g.bh), dim3(64), 0, s,
+                     g, bits, bits_t, count_t);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dq(const Geo& g, bool bf16, const void* q, const void* k,
+                              const void* v, const void* o, const void* dout, const float* lse,
+                              const int32_t* row_ptr, const int32_t* col_idx, float scale,
+                              void* dq, float* delta, hipStream_t s) {
+  return g.d == 64 ? launch_dq_t<64>(g, bf16, q, k, v, o, dout, lse, row_ptr, col_idx, scale, dq,
+                                     delta, s)
+                   : launch_dq_t<128>(g, bf16, q, k, v, o, dout, lse, row_ptr, col_idx, scale, dq,
+                                      delta, s);
+}
+
+hipError_t launch_attn_bwd_dkdv(const Geo& g, bool bf16, const void* q, const void* k,
+                                const void* v, const void* dout, const float* lse,
+                                const float* delta, const int32_t* col_ptr,
+                                const int32_t* row_idx, float scale, void* dk, void* dv,
+                                hipStream_t s) {
+  return g.d == 64 ? launch_dkdv_t<64>(g, bf16, q, k, v, dout, lse, delta, col_ptr, row_idx, scale,
+                                       dk, dv, s)
+                   : launch_dkdv_t<128>(g, bf16, q, k, v, dout, lse, delta, col_ptr, row_idx,
+                                        scale, dk, dv, s);
+}
+
+}  // namespace nabla

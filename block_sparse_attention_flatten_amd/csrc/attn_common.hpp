@@ -30,6 +30,34 @@ __device__ inline void pair_of(const Geo& g, int p, int* a, int* b) {
   *b = 2 * wp + 1 < g.gw ? *a + 1 : -1;
 }
 
+// Ascending list of one row of a CSR structure (a query block's kept key
+// blocks, or a key block's query blocks in the transposed mask), read through
+// the scalar cache (the constant address space makes these uniform reads
+// scalar loads); entries outside [0, nb) are skipped so a malformed list
+// cannot cause wild reads.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+struct KeptList {
+  const_i32* p;
+  int i, n, nb;
+  int head;                          // p[i] (first valid entry from i on), INT_MAX at the end
+  __device__ void settle() {
+    while (i < n && (unsigned)p[i] >= (unsigned)nb) ++i;
+    head = i < n ? p[i] : INT_MAX;
+  }
+};
+
+__device__ inline KeptList kept_list(const int32_t* row_ptr, const int32_t* cols, int nb, int q) {
+  KeptList l = {(const_i32*)cols, 0, 0, nb, INT_MAX};
+  if (q < 0) return l;
+  const int begin = ((const_i32*)row_ptr)[q];
+  const int end = ((const_i32*)row_ptr)[q + 1];
+  if (begin < 0 || end < begin || end > nb * nb) return l;   // malformed row: no keys
+  l.p = (const_i32*)(cols + begin);
+  l.n = end - begin;
+  l.settle();
+  return l;
+}
+
 // Workgroup id -> (head, pair item).  Workgroups are dispatched in id order,
 // round-robin over the 8 XCDs (XCD = id % 8).  Each head's items are cut into
 // 8 contiguous chunks and XCD x takes chunk (x + h) % 8 of head h: all XCDs

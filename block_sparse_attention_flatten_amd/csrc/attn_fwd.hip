@@ -51,39 +51,13 @@ struct AttnShape {
   static constexpr int kDTiles = D / 32;          // 32-row tiles of O^T
 };
 
-// Ascending kept list of one query block, read through the scalar cache (the
-// constant address space makes these uniform reads scalar loads); entries
-// outside [0, nb) are skipped so a malformed list cannot cause wild reads.
-typedef const __attribute__((address_space(4))) int32_t const_i32;
-struct KeptList {
-  const_i32* p;
-  int i, n, nb;
-  int head;                          // p[i] (first valid entry from i on), INT_MAX at the end
-  __device__ void settle() {
-    while (i < n && (unsigned)p[i] >= (unsigned)nb) ++i;
-    head = i < n ? p[i] : INT_MAX;
-  }
-};
-
-__device__ inline KeptList kept_list(const int32_t* row_ptr, const int32_t* cols, int nb, int q) {
-  KeptList l = {(const_i32*)cols, 0, 0, nb, INT_MAX};
-  if (q < 0) return l;
-  const int begin = ((const_i32*)row_ptr)[q];
-  const int end = ((const_i32*)row_ptr)[q + 1];
-  if (begin < 0 || end < begin || end > nb * nb) return l;   // malformed row: no keys
-  l.p = (const_i32*)(cols + begin);
-  l.n = end - begin;
-  l.settle();
-  return l;
-}
-
 // V is in the Q/K layout; its matrix-core operands come from transpose loads.
 template <int D, typename OutT>
 __global__ void __launch_bounds__(256, 2)
 attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const int32_t* __restrict__ row_ptr,
                      const int32_t* __restrict__ col_idx, float scale_log2,
-                     OutT* __restrict__ O) {
+                     OutT* __restrict__ O, float* __restrict__ lse) {
   using A = AttnShape<D>;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[kN * A::kStride];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[kN * A::kVStride];
@@ -290,6 +264,9 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
   // ---- normalise and write this lane's query row ----
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (lse != nullptr && myq >= 0 && hl == 0)   // ln sum exp(s * scale) = (m + log2 l) ln 2
+    lse[(head * nb + myq) * kN + qs] =
+        qvalid && l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
   if (myq >= 0 && (qvalid || g.layout == 1)) {
     OutT* orow = O + qoff;
     const float sc = qvalid ? inv : 0.f;
@@ -312,7 +289,8 @@ template <int D>
 __global__ void __launch_bounds__(64)
 attn_fwd_f32_kernel(const Geo g, const float* __restrict__ Q, const float* __restrict__ K,
                     const float* __restrict__ V, const int32_t* __restrict__ row_ptr,
-                    const int32_t* __restrict__ col_idx, float scale, float* __restrict__ O) {
+                    const int32_t* __restrict__ col_idx, float scale, float* __restrict__ O,
+                    float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) float Kt[kN * D];
   __shared__ __attribute__((aligned(16))) float Vt[kN * D];
   const int nb = g.nb;
@@ -371,6 +349,8 @@ attn_fwd_f32_kernel(const Geo g, const float* __restrict__ Q, const float* __res
       m = m_new;
     }
   }
+  if (lse != nullptr)
+    lse[(head * nb + qb) * kN + s] = qvalid && l > 0.f ? m + logf(l) : -INFINITY;
   if (qvalid || g.layout == 1) {
     const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
@@ -381,45 +361,45 @@ attn_fwd_f32_kernel(const Geo g, const float* __restrict__ Q, const float* __res
 template <int D, typename OutT>
 void launch_bf16(const Geo& g, const void* q, const void* k, const void* v,
                  const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
-                 hipStream_t s) {
+                 float* lse, hipStream_t s) {
   const float sl2 = scale * 1.4426950408889634f;   // softmax in base 2
   const int64_t chunk = (pair_items(g) + 7) / 8;
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OutT>), dim3((unsigned)(8 * chunk * g.bh)),
                      dim3(AttnShape<D>::kThreads), 0, s, g, (const __bf16*)q, (const __bf16*)k,
-                     (const __bf16*)v, row_ptr, col_idx, sl2, (OutT*)o);
+                     (const __bf16*)v, row_ptr, col_idx, sl2, (OutT*)o, lse);
 }
 
 void launch_bf16_any(const Geo& g, bool out_bf16, const void* q, const void* k, const void* v,
                      const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
-                     hipStream_t s) {
+                     float* lse, hipStream_t s) {
   if (g.d == 64) {
-    out_bf16 ? launch_bf16<64, __bf16>(g, q, k, v, row_ptr, col_idx, scale, o, s)
-             : launch_bf16<64, float>(g, q, k, v, row_ptr, col_idx, scale, o, s);
+    out_bf16 ? launch_bf16<64, __bf16>(g, q, k, v, row_ptr, col_idx, scale, o, lse, s)
+             : launch_bf16<64, float>(g, q, k, v, row_ptr, col_idx, scale, o, lse, s);
   } else {
-    out_bf16 ? launch_bf16<128, __bf16>(g, q, k, v, row_ptr, col_idx, scale, o, s)
-             : launch_bf16<128, float>(g, q, k, v, row_ptr, col_idx, scale, o, s);
+    out_bf16 ? launch_bf16<128, __bf16>(g, q, k, v, row_ptr, col_idx, scale, o, lse, s)
+             : launch_bf16<128, float>(g, q, k, v, row_ptr, col_idx, scale, o, lse, s);
   }
 }
 
 template <int D>
 void launch_f32(const Geo& g, const void* q, const void* k, const void* v,
                 const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
-                hipStream_t s) {
+                float* lse, hipStream_t s) {
   hipLaunchKernelGGL(attn_fwd_f32_kernel<D>, dim3((unsigned)(g.bh * g.nb)), dim3(64), 0, s, g,
                      (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx, scale,
-                     (float*)o);
+                     (float*)o, lse);
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const Geo& g, bool bf16, bool out_bf16, const void* q, const void* k,
                            const void* v, const int32_t* row_ptr, const int32_t* col_idx,
-                           float scale, void* o, hipStream_t s) {
+                           float scale, void* o, float* lse, hipStream_t s) {
   if (bf16) {
-    launch_bf16_any(g, out_bf16, q, k, v, row_ptr, col_idx, scale, o, s);
+    launch_bf16_any(g, out_bf16, q, k, v, row_ptr, col_idx, scale, o, lse, s);
   } else {
-    g.d == 64 ? launch_f32<64>(g, q, k, v, row_ptr, col_idx, scale, o, s)
-              : launch_f32<128>(g, q, k, v, row_ptr, col_idx, scale, o, s);
+    g.d == 64 ? launch_f32<64>(g, q, k, v, row_ptr, col_idx, scale, o, lse, s)
+              : launch_f32<128>(g, q, k, v, row_ptr, col_idx, scale, o, lse, s);
   }
   return hipGetLastError();
 }

@@ -124,7 +124,7 @@ __global__ void __launch_bounds__(256, 2)
 attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ VT, const int32_t* __restrict__ row_ptr,
                    const int32_t* __restrict__ col_idx, float scale_log2,
-                   OutT* __restrict__ O) {
+                   OutT* __restrict__ O, float* __restrict__ lse) {
   using S = VtShape<D>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   char* const kbuf = smem;                          // [2][kKBytes]
@@ -525,6 +525,9 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   bool ovalid;
   const int64_t ooff = query_row(&ovalid);
+  if (lse != nullptr && myq >= 0 && hl == 0)   // ln sum exp(s * scale) = (m + log2 l) ln 2
+    lse[(head * nb + myq) * kN + qs] =
+        ovalid && l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
   if (myq >= 0 && (ovalid || g.layout == 1)) {
     OutT* orow = O + ooff;
     const float sc = ovalid ? inv : 0.f;
@@ -543,7 +546,7 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
 template <int D, typename OutT>
 hipError_t launch_vt(const Geo& g, const void* q, const void* k, const void* vt,
                      const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
-                     hipStream_t s) {
+                     float* lse, hipStream_t s) {
   using S = VtShape<D>;
   const int nw = (g.nb + 31) >> 5;
   const size_t lds = S::kBufBytes + (size_t)(2 * nw + 1) * 4 + (size_t)g.nb * 2;
@@ -555,7 +558,7 @@ hipError_t launch_vt(const Geo& g, const void* q, const void* k, const void* vt,
   const int64_t chunk = (pair_items(g) + 7) / 8;
   hipLaunchKernelGGL(kern, dim3((unsigned)(8 * chunk * g.bh)), dim3(256), lds, s, g,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)vt, row_ptr, col_idx,
-                     sl2, (OutT*)o);
+                     sl2, (OutT*)o, lse);
   return hipGetLastError();
 }
 
@@ -563,12 +566,12 @@ hipError_t launch_vt(const Geo& g, const void* q, const void* k, const void* vt,
 
 hipError_t launch_attn_fwd_vt(const Geo& g, bool out_bf16, const void* q, const void* k,
                               const void* vt, const int32_t* row_ptr, const int32_t* col_idx,
-                              float scale, void* o, hipStream_t s) {
+                              float scale, void* o, float* lse, hipStream_t s) {
   if (g.d == 64)
-    return out_bf16 ? launch_vt<64, __bf16>(g, q, k, vt, row_ptr, col_idx, scale, o, s)
-                    : launch_vt<64, float>(g, q, k, vt, row_ptr, col_idx, scale, o, s);
-  return out_bf16 ? launch_vt<128, __bf16>(g, q, k, vt, row_ptr, col_idx, scale, o, s)
-                  : launch_vt<128, float>(g, q, k, vt, row_ptr, col_idx, scale, o, s);
+    return out_bf16 ? launch_vt<64, __bf16>(g, q, k, vt, row_ptr, col_idx, scale, o, lse, s)
+                    : launch_vt<64, float>(g, q, k, vt, row_ptr, col_idx, scale, o, lse, s);
+  return out_bf16 ? launch_vt<128, __bf16>(g, q, k, vt, row_ptr, col_idx, scale, o, lse, s)
+                  : launch_vt<128, float>(g, q, k, vt, row_ptr, col_idx, scale, o, lse, s);
 }
 
 }  // namespace nabla

@@ -98,12 +98,26 @@ hipError_t launch_mask(const Geo& g, const float* qbar, const float* kbar, float
                        hipStream_t s);
 hipError_t launch_compact(const Geo& g, const uint32_t* bits, const int32_t* cnt,
                           int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
+// lse (nullable): float32 [bh, nb, 64] natural-log log-sum-exp of each query's
+// scaled scores over its kept valid keys; -inf for pad slots and empty rows
 hipError_t launch_attn_fwd(const Geo& g, bool bf16, bool out_bf16, const void* q, const void* k,
                            const void* v, const int32_t* row_ptr, const int32_t* col_idx,
-                           float scale, void* o, hipStream_t s);
+                           float scale, void* o, float* lse, hipStream_t s);
 hipError_t launch_transpose_v(const Geo& g, const void* v, void* vt, hipStream_t s);
+// gradients (attn_bwd.hip); lse / delta float32 [bh, nb, 64]
+hipError_t launch_mask_transpose(const Geo& g, const uint32_t* bits, uint32_t* bits_t,
+                                 int32_t* count_t, hipStream_t s);
+hipError_t launch_attn_bwd_dq(const Geo& g, bool bf16, const void* q, const void* k,
+                              const void* v, const void* o, const void* dout, const float* lse,
+                              const int32_t* row_ptr, const int32_t* col_idx, float scale,
+                              void* dq, float* delta, hipStream_t s);
+hipError_t launch_attn_bwd_dkdv(const Geo& g, bool bf16, const void* q, const void* k,
+                                const void* v, const void* dout, const float* lse,
+                                const float* delta, const int32_t* col_ptr,
+                                const int32_t* row_idx, float scale, void* dk, void* dv,
+                                hipStream_t s);
 hipError_t launch_attn_fwd_vt(const Geo& g, bool out_bf16, const void* q, const void* k,
                               const void* vt, const int32_t* row_ptr, const int32_t* col_idx,
-                              float scale, void* o, hipStream_t s);
+                              float scale, void* o, float* lse, hipStream_t s);
 
 }  // namespace nabla

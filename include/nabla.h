@@ -21,6 +21,15 @@
  *   nabla_unflatten   inverse reorder of the output
  *   nabla_forward     pool -> mask -> compact -> (transpose_v) -> attn_fwd in one call
  *
+ * Gradients with the kept-block mask held fixed (training with NABLA:
+ * [GZ] core contributions and experimental results 2, pre-training;
+ * [LS] sec. 3):
+ *   nabla_attn_fwd_lse / nabla_attn_fwd_vt_lse   forward that also writes the
+ *                     log-sum-exp of every query's scores
+ *   nabla_mask_transpose  key-major (transposed) mask, compacted by nabla_compact
+ *   nabla_attn_bwd_dq     dQ and D = rowsum(dO * O), query-block lists
+ *   nabla_attn_bwd_dkdv   dK and dV, key-block (transposed) lists
+ *
  * Conventions for every entry point
  *   - All pointers except `geom`, `sta` and `bytes`/`offsets` outputs are
  *     DEVICE pointers, allocated and owned by the caller.  The library
@@ -71,7 +80,7 @@
 extern "C" {
 #endif
 
-#define NABLA_ABI_VERSION 1
+#define NABLA_ABI_VERSION 2
 
 enum nabla_status {
   NABLA_OK = 0,
@@ -183,6 +192,57 @@ int nabla_transpose_v(const nabla_geom* geom, const void* v, void* vt, void* str
 int nabla_attn_fwd_vt(const nabla_geom* geom, const void* q, const void* k,
                       const void* vt, const int32_t* row_ptr, const int32_t* col_idx,
                       float scale, void* o, void* stream);
+
+/* Gradients ([GZ] core contributions, "dual-stage acceleration" of training
+ * and inference, and experimental results 2, pre-training a 2B DiT with
+ * NABLA; [LS] sec. 3).  The kept-block mask is a threshold on pooled scores,
+ * so it is held fixed and only the exact attention over the kept blocks is
+ * differentiated: with p = softmax(q k^T * scale) over the kept valid keys,
+ * o = p v and incoming gradient dO,
+ *   dV = p^T dO,  dP = dO V^T,  dS = p (dP - D),  D = rowsum(dO * o),
+ *   dQ = dS K * scale,  dK = dS^T Q * scale.
+ * Shared conventions: lse and delta are float32 [B, heads, nb, 64], indexed by
+ * block and slot (slot = row-in-patch * 8 + column-in-patch) whatever the
+ * tensor layout; the gradient calls need geom->out_dtype == geom->dtype
+ * (NABLA_E_DTYPE otherwise), and o, dout, dq, dk, dv are in geom's layout and
+ * dtype.  Pad slots of dq, dk, dv are not written in the THW layout and are
+ * written as zeros in the blocked layout.  bf16 inputs use bf16 matrix cores
+ * with float32 accumulation; float32 inputs compute in float32. */
+
+/* nabla_attn_fwd that also writes lse[b, h, c, slot] = ln sum_j exp(s_j),
+ * s_j = q . k_j * scale over the query's kept valid keys (-inf for pad slots
+ * and for rows with no keys).  lse must not be NULL. */
+int nabla_attn_fwd_lse(const nabla_geom* geom, const void* q, const void* k,
+                       const void* v, const int32_t* row_ptr, const int32_t* col_idx,
+                       float scale, void* o, float* lse, void* stream);
+
+/* nabla_attn_fwd_vt with the lse output of nabla_attn_fwd_lse (bf16 only). */
+int nabla_attn_fwd_vt_lse(const nabla_geom* geom, const void* q, const void* k,
+                          const void* vt, const int32_t* row_ptr, const int32_t* col_idx,
+                          float scale, void* o, float* lse, void* stream);
+
+/* Transposed mask: bit r of mask_bits_t[b, h, c, :] = bit c of
+ * mask_bits[b, h, r, :], i.e. row c lists the query blocks that keep key
+ * block c; row_count_t[b, h, c] = its number of set bits.  Shapes as
+ * mask_bits / row_count.  nabla_compact on the result gives the key-major
+ * lists (col_ptr, row_idx) of nabla_attn_bwd_dkdv.  Bit-exact. */
+int nabla_mask_transpose(const nabla_geom* geom, const uint32_t* mask_bits,
+                         uint32_t* mask_bits_t, int32_t* row_count_t, void* stream);
+
+/* dq and delta (D) from q, k, v, the forward's o and lse, and dout, over the
+ * query-major lists (row_ptr, col_idx) of the forward. */
+int nabla_attn_bwd_dq(const nabla_geom* geom, const void* q, const void* k,
+                      const void* v, const void* o, const void* dout, const float* lse,
+                      const int32_t* row_ptr, const int32_t* col_idx, float scale,
+                      void* dq, float* delta, void* stream);
+
+/* dk and dv over the key-major lists (col_ptr [B*heads, nb+1], row_idx
+ * [B*heads, nb*nb]) of the transposed mask; delta from nabla_attn_bwd_dq
+ * (so this call follows it on the stream). */
+int nabla_attn_bwd_dkdv(const nabla_geom* geom, const void* q, const void* k,
+                        const void* v, const void* dout, const float* lse,
+                        const float* delta, const int32_t* col_ptr, const int32_t* row_idx,
+                        float scale, void* dk, void* dv, void* stream);
 
 /* Workspace for nabla_forward and the byte offsets of its parts, in order:
  * offsets[0] qbar, [1] kbar, [2] mask_bits, [3] row_count, [4] row_ptr,

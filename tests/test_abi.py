@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, f"{name} not exported"
         assert getattr(lib, name) is not None
-    assert lib.nabla_abi_version() == 1
+    assert lib.nabla_abi_version() == 2
 
 
 def G(**kw):
