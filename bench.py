@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--sta", type=str, default=None, help="e.g. 3,3,3 or 0,0,0")
     ap.add_argument("--heads", type=int, default=None, help="override the head count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the gradient calls (dq, dk, dv with the mask held fixed)")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense reference (the same kernel with every block kept)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -347,6 +349,45 @@ def main():
                                       int(per_row.max())],
         "gpu": torch.cuda.get_device_name(0),
     }
+    if not args.no_backward:
+        # gradients with the mask held fixed: the forward with its log-sum-exp,
+        # the key-major lists, then dQ (and D) and dK/dV; incoming gradient
+        # dO is a synthetic field of the same shape
+        dout = synth.make_tensor(cfg, 3, device="cuda")
+        lse = torch.empty(nabla.lse_shape(g), dtype=torch.float32, device=dev)
+        if vt_path:
+            nabla.nabla_attn_fwd_vt_lse(g, q, k, vt, rp, ci, scale, o, lse, stream)
+        else:
+            nabla.nabla_attn_fwd_lse(g, q, k, v, rp, ci, scale, o, lse, stream)
+        bits_t = torch.empty_like(bits)
+        cnt_t = torch.empty_like(cnt)
+        cp = torch.empty_like(rp)
+        ri = torch.empty_like(ci)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        delta = torch.empty_like(lse)
+        bstages = {
+            "mask_transpose": time_call(lambda: nabla.nabla_mask_transpose(g, bits, bits_t,
+                                                                           cnt_t, stream)),
+            "compact_transposed": time_call(lambda: nabla.nabla_compact(g, bits_t, cnt_t, cp, ri,
+                                                                        stream)),
+            "dq": time_call(lambda: nabla.nabla_attn_bwd_dq(g, q, k, v, o, dout, lse, rp, ci,
+                                                            scale, dq, delta, stream), reps=3),
+            "dkdv": time_call(lambda: nabla.nabla_attn_bwd_dkdv(g, q, k, v, dout, lse, delta, cp,
+                                                                ri, scale, dk, dv, stream),
+                              reps=3),
+        }
+        bwd_ms = sum(bstages.values())
+        bwd_flops = 2.5 * kept_flops         # five 64x64xd products per kept pair vs two
+        result["backward"] = {
+            "what": "dq, dk, dv with the mask held fixed (transposed lists + dQ + dK/dV)",
+            "ms": round(bwd_ms, 3),
+            "stages_ms": {k_: round(v_, 4) for k_, v_ in bstages.items()},
+            "algorithmic_tflop": round(bwd_flops / 1e12, 3),
+            "tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 1),
+            "frac": round(bwd_flops / (bwd_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        }
+        log(f"backward: {bwd_ms:.2f} ms {bstages}")
+        del dout, lse, bits_t, cnt_t, cp, ri, dq, dk, dv, delta
     if not args.no_dense:
         # dense reference: the same attention kernel with every block kept (the
         # mask of thr = 1 without STA), i.e. full attention over all valid keys

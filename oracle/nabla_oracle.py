@@ -271,7 +271,8 @@ def block_sparse_attention(qb: np.ndarray, kb: np.ndarray, vb: np.ndarray,
 # ---------------------------------------------------------------------------
 def block_sparse_attention_backward(qb: np.ndarray, kb: np.ndarray, vb: np.ndarray,
                                     m: np.ndarray, valid: np.ndarray, dob: np.ndarray,
-                                    scale: Optional[float] = None):
+                                    scale: Optional[float] = None,
+                                    rows: Optional[Iterable[int]] = None):
     """One head: gradients of L = sum(dob * o) for o = block_sparse_attention(...).
 
     The kept-block mask is a piecewise-constant function of q and k (a
@@ -284,7 +285,10 @@ def block_sparse_attention_backward(qb: np.ndarray, kb: np.ndarray, vb: np.ndarr
     qb, kb, vb, dob: [nb, N, d]; m: [nb, nb] bool; valid: [nb, N] bool.
     Returns dq, dk, dv [nb, N, d] float64 (zero at pad slots) and lse [nb, N],
     the natural-log log-sum-exp of each valid query's scores (-inf for pad
-    queries and for rows without keys).
+    queries and for rows without keys).  With ``rows``, only those query blocks
+    are processed: their dq and lse are exact, and dk, dv hold their
+    contributions only (exact for a key block when rows covers every query
+    block that keeps it).
     """
     qb = np.asarray(qb, dtype=np.float64)
     kb = np.asarray(kb, dtype=np.float64)
@@ -297,7 +301,7 @@ def block_sparse_attention_backward(qb: np.ndarray, kb: np.ndarray, vb: np.ndarr
     dv = np.zeros((nb, N, d))
     lse = np.full((nb, N), -np.inf)
     slot = np.arange(N)
-    for a in range(nb):
+    for a in (range(nb) if rows is None else rows):
         cols = np.flatnonzero(m[a])
         kblk = np.repeat(cols, N)[valid[cols].ravel()]          # key token -> block
         kslot = np.tile(slot, len(cols))[valid[cols].ravel()]   # key token -> slot
@@ -316,8 +320,9 @@ def block_sparse_attention_backward(qb: np.ndarray, kb: np.ndarray, vb: np.ndarr
         dp = do @ vals.T
         ds = p * (dp - (do * o).sum(axis=1, keepdims=True))
         dq[a, qi] = (ds @ keys) * scale
-        np.add.at(dk, (kblk, kslot), (ds.T @ q) * scale)
-        np.add.at(dv, (kblk, kslot), p.T @ do)
+        # each key token appears once in a row's list: a plain indexed add
+        dk[kblk, kslot] += (ds.T @ q) * scale
+        dv[kblk, kslot] += p.T @ do
     return dq, dk, dv, lse
 
 

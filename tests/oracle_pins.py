@@ -364,6 +364,20 @@ def pin_backward_autograd(O):
         assert np.all(np.isneginf(lse.reshape(-1)[~vq]))
 
 
+def pin_backward_rows_subset(O):
+    """Restricting to the query blocks that keep key block c reproduces c's
+    full dk, dv and those rows' dq (the sums are the same terms)."""
+    rng = _rng(14)
+    g, valid, qb, kb, vb, dob, m = _bwd_case(O, rng, 2, 16, 16, 8, 0.35)
+    dq, dk, dv, lse = O.block_sparse_attention_backward(qb, kb, vb, m, valid, dob)
+    c = 3
+    rows = np.flatnonzero(m[:, c])
+    sq, sk, sv, sl = O.block_sparse_attention_backward(qb, kb, vb, m, valid, dob, rows=rows)
+    assert np.abs(sk[c] - dk[c]).max() < 1e-12 and np.abs(sv[c] - dv[c]).max() < 1e-12
+    assert np.abs(sq[rows] - dq[rows]).max() < 1e-12
+    assert np.array_equal(sl[rows], lse[rows])
+
+
 def pin_backward_invariants(O):
     """Rows of p sum to 1, so the dv rows add up to the do rows; rows of ds sum
     to 0, so the dk rows add up to 0 (per head)."""
