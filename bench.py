@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--sta", type=str, default=None, help="e.g. 3,3,3 or 0,0,0")
     ap.add_argument("--heads", type=int, default=None, help="override the head count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--thr-sweep", default="0,0.5,0.7,0.9",
+                    help="thresholds for the sparsity/speed sweep (0 = pure STA); '' skips it")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the gradient calls (dq, dk, dv with the mask held fixed)")
     ap.add_argument("--no-dense", action="store_true",
@@ -349,6 +351,25 @@ def main():
                                       int(per_row.max())],
         "gpu": torch.cuda.get_device_name(0),
     }
+    if args.thr_sweep:
+        # sparsity and attention time against thr with the same inputs and STA
+        # window; thr = 0 is the pure STA mask (adaptive part off)
+        sweep = []
+        for t in [float(x) for x in args.thr_sweep.split(",")]:
+            if t == 0.0 and not any(sta):
+                continue
+            nabla.nabla_mask(g, qbar, kbar, t, sta, bits, cnt, None, stream)
+            nabla.nabla_compact(g, bits, cnt, rp, ci, stream)
+            t_ms = time_call(attention, reps=3)
+            n_t = int(cnt.to(torch.int64).sum())
+            f_t = n_t * 4 * 64 * 64 * d
+            sweep.append({"thr": t, "sparsity": round(1.0 - n_t / (B * h * nb * nb), 4),
+                          "attn_ms": round(t_ms, 3),
+                          "tflops": round(f_t / (t_ms * 1e-3) / 1e12, 1)})
+        result["thr_sweep"] = sweep
+        log(f"thr sweep: {sweep}")
+        step()                       # restore the call's own mask and lists
+        torch.cuda.synchronize()
     if not args.no_backward:
         # gradients with the mask held fixed: the forward with its log-sum-exp,
         # the key-major lists, then dQ (and D) and dK/dV; incoming gradient

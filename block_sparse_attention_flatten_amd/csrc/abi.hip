@@ -70,7 +70,11 @@ int check_sta(const int32_t* sta, int out[3]) {
   return NABLA_OK;
 }
 
-bool thr_ok(float thr) { return isfinite(thr) && thr > 0.0f && thr <= 1.0f; }
+// thr in (0, 1]; 0 (adaptive part off, pure STA) only with an STA window
+bool thr_ok(float thr, const int win[3]) {
+  if (!isfinite(thr) || thr < 0.0f || thr > 1.0f) return false;
+  return thr > 0.0f || win[0] > 0;
+}
 bool scale_ok(float s) { return isfinite(s) && s > 0.0f; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -148,7 +152,7 @@ const char* nabla_status_string(int status) {
     case NABLA_E_DTYPE: return "dtype/out_dtype must be F32 or BF16 (F32 inputs need F32 output)";
     case NABLA_E_HEAD_DIM: return "head_dim must be 64 or 128";
     case NABLA_E_PATCH: return "patch side P must be 8";
-    case NABLA_E_THR: return "thr must be finite and in (0, 1]";
+    case NABLA_E_THR: return "thr must be finite and in (0, 1], or 0 with an STA window";
     case NABLA_E_STA: return "STA window must be {0,0,0} or three positive odd sizes";
     case NABLA_E_WORKSPACE: return "workspace smaller than nabla_forward_workspace_size";
     case NABLA_E_LAYOUT: return "layout must be NABLA_LAYOUT_THW or NABLA_LAYOUT_BLOCKED";
@@ -210,10 +214,10 @@ int nabla_mask(const nabla_geom* geom, const float* qbar, const float* kbar, flo
   bool empty;
   int st = make_geo(geom, false, &g, &empty);
   if (st != NABLA_OK) return st;
-  if (!thr_ok(thr)) return NABLA_E_THR;
   int win[3];
   st = check_sta(sta, win);
   if (st != NABLA_OK) return st;
+  if (!thr_ok(thr, win)) return NABLA_E_THR;
   if (empty) return NABLA_OK;
   if (qbar == nullptr || kbar == nullptr || mask_bits == nullptr || row_count == nullptr)
     return NABLA_E_NULL;
@@ -342,11 +346,11 @@ int nabla_forward(const nabla_geom* geom, const void* q, const void* k, const vo
   bool empty;
   int st = make_geo(geom, true, &g, &empty);
   if (st != NABLA_OK) return st;
-  if (!thr_ok(thr)) return NABLA_E_THR;
   if (!scale_ok(scale)) return NABLA_E_SCALE;
   int win[3];
   st = check_sta(sta, win);
   if (st != NABLA_OK) return st;
+  if (!thr_ok(thr, win)) return NABLA_E_THR;
   if (empty) return NABLA_OK;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || workspace == nullptr)
     return NABLA_E_NULL;

@@ -178,7 +178,9 @@ __global__ void __launch_bounds__(R * 64) mask_kernel(const Geo g, const float* 
 
     // kept-set words: lane w holds words w and w + 64
     uint32_t kw0 = 0, kw1 = 0;
-    if (thr >= 1.0f) {
+    if (thr <= 0.0f) {
+      // adaptive part off (pure STA): nothing kept here
+    } else if (thr >= 1.0f) {
       for (int w = lane; w < nw; w += 64) {
         const int n = nb - 32 * w;
         const uint32_t v = n >= 32 ? 0xffffffffu : ((1u << n) - 1u);

@@ -89,7 +89,7 @@ enum nabla_status {
   NABLA_E_DTYPE = -3,       /* dtype / out_dtype not supported (see nabla_geom) */
   NABLA_E_HEAD_DIM = -4,    /* head_dim not 64 or 128 */
   NABLA_E_PATCH = -5,       /* P != 8 */
-  NABLA_E_THR = -6,         /* thr not in (0, 1] or not finite */
+  NABLA_E_THR = -6,         /* thr not in (0, 1] (or 0 without STA), or not finite */
   NABLA_E_STA = -7,         /* STA window not all-zero or all positive odd */
   NABLA_E_WORKSPACE = -8,   /* workspace smaller than nabla_forward_workspace_size */
   NABLA_E_LAYOUT = -9,      /* layout not NABLA_LAYOUT_THW / NABLA_LAYOUT_BLOCKED */
@@ -147,7 +147,9 @@ int nabla_pool(const nabla_geom* geom, const void* q, const void* k,
  * (thr = 1 keeps every block).  If sta = {wt, wh, ww} is non-zero, every
  * block within wt/2 frames, wh/2 block rows and ww/2 block columns of the
  * row's own block is added (window clipped at the borders).
- *   thr            in (0, 1]
+ *   thr            in (0, 1]; 0 turns the adaptive part off, which leaves
+ *                  the pure STA window ([GZ] experimental results 3, the
+ *                  static baseline) and needs a non-zero sta
  *   sta            host array of 3 ints; NULL or {0,0,0} = no STA;
  *                  otherwise three positive odd numbers
  *   mask_bits      out, uint32 [B, heads, nb, nw]: union mask

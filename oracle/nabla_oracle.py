@@ -29,7 +29,8 @@ design notes):
   * reduced map: scores q_bar . k_bar / sqrt(d), softmax along each row.
   * CDF cut: sort a row ascending, cumulate, keep blocks whose cumulative
     probability exceeds 1 - thr.  Equal probabilities: the lower block index is
-    treated as the more important one (kept first).  thr >= 1 keeps every block.
+    treated as the more important one (kept first).  thr >= 1 keeps every block;
+    thr = 0 keeps none (pure STA when combined with a window).
   * STA: a window of (wt, wh, ww) blocks centred on the query block in
     (frame, block-row, block-column) coordinates, clipped at the borders.
   * attention: pad keys never receive weight; pad queries produce zeros.
@@ -173,11 +174,14 @@ def cdf_keep_row(p: np.ndarray, thr: float) -> np.ndarray:
     The row is sorted ascending and cumulated; a block is kept when its
     cumulative probability exceeds 1 - thr.  Among equal probabilities the
     higher block index sorts first in ascending order, so the lower index is
-    kept first.  thr >= 1 keeps every block.
+    kept first.  thr >= 1 keeps every block; thr = 0 keeps none (with an STA
+    window this is the pure-STA mask, the pages' static baseline).
     """
     n = p.shape[0]
     if thr >= 1.0:
         return np.ones(n, dtype=bool)
+    if thr <= 0.0:
+        return np.zeros(n, dtype=bool)
     idx = np.arange(n)
     order = np.lexsort((-idx, p))          # ascending p; ties: descending index
     cdf = np.cumsum(p[order])
@@ -342,7 +346,7 @@ def band_rows(p: np.ndarray, m_ad: np.ndarray, thr: float, eps: float = 1e-5):
     flat_m = m_ad.reshape(-1, p.shape[-1])
     a = np.zeros(flat_p.shape[0], dtype=bool)
     b = np.zeros(flat_p.shape[0], dtype=bool)
-    if thr >= 1.0:
+    if thr >= 1.0 or thr <= 0.0:
         return a.reshape(p.shape[:-1]), b.reshape(p.shape[:-1])
     for i, (row, keep) in enumerate(zip(flat_p, flat_m)):
         kept = np.sort(row[keep])[::-1]

@@ -212,6 +212,18 @@ def pin_sta(O):
     assert not O.sta_mask(g, (0, 0, 0)).any()
 
 
+def pin_pure_sta(O):
+    """thr = 0 turns the adaptive part off: the mask is exactly the STA window
+    (the static baseline the pages compare against)."""
+    rng = _rng(15)
+    g = O.Geometry(3, 16, 24, 8)
+    qbar, kbar = rng.standard_normal((2, g.nb, 16))
+    for win in [(3, 3, 3), (1, 3, 5)]:
+        m, m_ad, _ = O.nabla_mask(qbar, kbar, 0.0, g, win)
+        assert not m_ad.any()
+        assert np.array_equal(m, O.sta_mask(g, win))
+
+
 def pin_union(O):
     rng = _rng(6)
     g = O.Geometry(3, 24, 32, 8)

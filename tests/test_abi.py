@@ -71,6 +71,11 @@ def test_argument_validation():
     assert lib.nabla_pool(ctypes.byref(g), None, FAKE, FAKE, FAKE, None) == -1
     for bad in [0.0, -0.1, 1.5, float("nan"), float("inf")]:
         assert lib.nabla_mask(ctypes.byref(g), FAKE, FAKE, bad, None, FAKE, FAKE, None, None) == -6
+    # thr = 0 (pure STA) needs a window; with one, validation passes on to the pointers
+    assert lib.nabla_mask(ctypes.byref(g), FAKE, FAKE, 0.0, sta(0, 0, 0), FAKE, FAKE, None,
+                          None) == -6
+    assert lib.nabla_mask(ctypes.byref(g), None, FAKE, 0.0, sta(3, 3, 3), FAKE, FAKE, None,
+                          None) == -1
     for bad in [(2, 3, 3), (3, 0, 3), (-1, 3, 3), (3, 3, 4)]:
         assert lib.nabla_mask(ctypes.byref(g), FAKE, FAKE, 0.5, sta(*bad), FAKE, FAKE, None,
                               None) == -7

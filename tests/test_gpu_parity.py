@@ -27,6 +27,7 @@ CASES = {
     "d64_bf16": ("small", dict(heads=2, T=4, H=24, W=40, head_dim=64, thr=0.8, sta=(3, 3, 3))),
     "thr_one": ("small", dict(heads=2, T=2, H=16, W=24, thr=1.0)),
     "thr_low": ("small", dict(heads=2, T=3, H=24, W=24, thr=0.05)),
+    "pure_sta": ("small", dict(heads=2, T=3, H=21, W=24, thr=0.0, sta=(3, 3, 3))),
 }
 
 
