@@ -185,7 +185,103 @@ __device__ inline void store_row(__bf16* dst, const f32x16 (&acc)[D / 32], float
                      acc[dt][4 * gq + 3] * mul);
 }
 
+// ---- swizzled tiles filled by direct-to-LDS loads ----
+// A 64 x D bf16 tile whose 16-byte chunks are permuted within each row so that
+// the 16-byte row reads of 16 consecutive rows (one logical chunk) hit
+// distinct banks: 256-byte rows (D = 128) use chunk ^ (r & 7) plus 128 bytes
+// of padding after every 8 rows; 128-byte rows (D = 64) use chunk ^
+// ((r & 7) ^ ((r >> 3) & 1)).  The tile is filled in 1-KB direct loads:
+// lane l of a load writes bytes 16 l .. 16 l + 15 of it and reads the global
+// chunk that belongs there.
+template <int D>
+struct SwTile {
+  static constexpr bool kWide = D == 128;
+  static constexpr int kGroupBytes = kWide ? 8 * 256 + 128 : 8 * 128;   // 8 rows
+  static constexpr int kBytes = 8 * kGroupBytes;
+  static constexpr int kOps = kN * D * 2 / 1024;          // 1-KB loads per tile
+  __device__ static int swz(int r) { return kWide ? (r & 7) : ((r & 7) ^ ((r >> 3) & 1)); }
+  // byte offset of logical chunk c of row r
+  __device__ static int addr(int r, int c) {
+    return (r >> 3) * kGroupBytes + (r & 7) * (2 * D) + ((c ^ swz(r)) << 4);
+  }
+  // load o: the row and logical chunk this lane moves, and the load's LDS offset
+  __device__ static void op_rc(int o, int lane, int* r, int* c) {
+    if (kWide) {
+      *r = 4 * o + (lane >> 4);
+      *c = (lane & 15) ^ swz(*r);
+    } else {
+      *r = 8 * o + (lane >> 3);
+      *c = (lane & 7) ^ swz(*r);
+    }
+  }
+  __device__ static int op_dst(int o) {
+    return kWide ? (o >> 1) * kGroupBytes + (o & 1) * 1024 : o * 1024;
+  }
+};
+
+// Wavefront `wave`'s share (kOps / 4 loads) of the tile of block blk of the
+// tensor behind rs into the tile at LDS byte address dst.  Pad rows of a
+// latent-edge block load row 0 of the block.
+template <int D>
+__device__ inline void dma_tile(const Geo& g, __amdgpu_buffer_rsrc_t rs, int row_step, int blk,
+                                int wave, int lane, char* dst) {
+  using T = SwTile<D>;
+  const BlockCoord bc = block_coord(g, blk);
+  const int rv = block_rows_valid(g, bc), cv = block_cols_valid(g, bc);
+  const uint32_t sb = 2u * (uint32_t)block_base(g, blk, bc);
+#pragma unroll
+  for (int i = 0; i < T::kOps / 4; ++i) {
+    const int o = wave * (T::kOps / 4) + i;
+    int r, c;
+    T::op_rc(o, lane, &r, &c);
+    const bool ok = (r >> 3) < rv && (r & 7) < cv;
+    const int el = (ok ? (r >> 3) * row_step + (r & 7) * D : 0) + c * 8;
+    dma16(rs, 2u * (uint32_t)el, sb, dst + T::op_dst(o));
+  }
+}
+
+// 32 x 32 product over d with tile rows row0 + jl as the A operand (16-byte
+// row reads of a swizzled tile at LDS address tb) and op as the B operand.
+template <int D>
+__device__ inline f32x16 sw_rows_times(int tb, int row0, int jl, int hl,
+                                       const bf16x8 (&op)[D / 16]) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const bf16x8 a = lds_read16(tb + SwTile<D>::addr(row0 + jl, 2 * s + hl));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, op[s], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// acc[dt] += T^T * B over tile rows row0 .. row0 + 31 (see cols_times), the
+// transpose loads addressing the swizzled tile at LDS address tb.
+template <int D>
+__device__ inline void sw_cols_times(int tb, int row0, int lane, int hl, const bf16x8 (&bop)[2],
+                                     f32x16 (&acc)[D / 32]) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const int rsub = (lane & 15) >> 2;
+  const int csub = (lane & 16) + 4 * (lane & 3);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int col = 32 * dt + csub;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = row0 + 16 * h + 4 * hl + rsub;
+      const int lo_a = tb + SwTile<D>::addr(r, col >> 3) + (col & 7) * 2;
+      const int hi_a = tb + SwTile<D>::addr(r + 8, col >> 3) + (col & 7) * 2;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)lo_a);
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)hi_a);
+      const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop[h], acc[dt], 0, 0, 0);
+    }
+  }
+}
+
 // ---- dQ (and D) ----
+// K and V tiles move by direct-to-LDS loads into two buffers each: step s
+// loads the next union block's tiles while computing on the current ones,
+// with one barrier per step.
 template <int D>
 __global__ void __launch_bounds__(256, 2)
 attn_bwd_dq_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
@@ -195,8 +291,8 @@ attn_bwd_dq_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
                    float scale_log2, float scale, __bf16* __restrict__ dQ,
                    float* __restrict__ delta) {
   using A = BwdShape<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[kN * A::kStride];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[kN * A::kStride];
+  using T = SwTile<D>;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];   // K[2], V[2] tiles
 
   const int nb = g.nb;
   const int items = pair_items(g);
@@ -208,13 +304,16 @@ attn_bwd_dq_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 1;
   const int hl = lane >> 5;
   const int jl = lane & 31;
   const int myq = grp == 0 ? qa : qpair;
   const int64_t hoff = head * (int64_t)g.head_elems;
   const int row_step = block_row_step(g);
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(K + hoff, 2u * (uint32_t)g.head_elems);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(V + hoff, 2u * (uint32_t)g.head_elems);
+  const int lds0 = (int)(uintptr_t)(lds_char*)smem;
 
   // this lane's query row: Q and dO as B operands, D = rowsum(dO * O)
   const int qs = 32 * (wave & 1) + jl;
@@ -255,42 +354,46 @@ attn_bwd_dq_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
   const int32_t* cols = col_idx + head * (int64_t)nb * nb;
   KeptList la = kept_list(rp, cols, nb, qa);
   KeptList lb = kept_list(rp, cols, nb, qpair);
-  TilePair<D> pre;
-  int next = min(la.head, lb.head);
-  if (next != INT_MAX) pre.fetch(g, K, V, hoff, row_step, next, tid);
-  while (next != INT_MAX) {
-    const int beta = next;
-    const bool in_a = la.head == beta;
-    const bool in_b = lb.head == beta;
+  auto load = [&](int blk, int buf) {
+    dma_tile<D>(g, krs, row_step, blk, wave, lane, smem + buf * T::kBytes);
+    dma_tile<D>(g, vrs, row_step, blk, wave, lane, smem + (2 + buf) * T::kBytes);
+  };
+  int cur = min(la.head, lb.head);           // current block of the merged union
+  if (cur != INT_MAX) load(cur, 0);
+  for (int s = 0; cur != INT_MAX; ++s) {
+    const bool in_a = la.head == cur;
+    const bool in_b = lb.head == cur;
     if (in_a) { ++la.i; la.settle(); }
     if (in_b) { ++lb.i; lb.settle(); }
-    next = min(la.head, lb.head);
-    __syncthreads();                 // every wavefront is done with the previous tiles
-    pre.put(Ks, Vs, tid);
-    __syncthreads();
-    if (next != INT_MAX) pre.fetch(g, K, V, hoff, row_step, next, tid);
-    if (!(grp == 0 ? in_a : in_b)) continue;   // wavefront-uniform: not a kept block of ours
-
-    const BlockCoord bc = block_coord(g, beta);
-    const int rv = block_rows_valid(g, bc);
-    const int cv = block_cols_valid(g, bc);
+    const int next = min(la.head, lb.head);
+    wait_vmcnt0();                   // this wavefront's loads of cur have landed
+    __syncthreads();                 // ... everyone's, and everyone is done with the other buffer
+    if (next != INT_MAX) load(next, (s + 1) & 1);
+    if (grp == 0 ? in_a : in_b) {    // wavefront-uniform: a kept block of ours
+      const int kb = lds0 + (s & 1) * T::kBytes;
+      const int vb = lds0 + (2 + (s & 1)) * T::kBytes;
+      const BlockCoord bc = block_coord(g, cur);
+      const int rv = block_rows_valid(g, bc);
+      const int cv = block_cols_valid(g, bc);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      // S^T and dP^T for keys 32 kt .. 32 kt + 31 (rows) of this lane's query
-      const f32x16 sacc = rows_times<D>(Ks, 32 * kt, jl, hl, qop);
-      const f32x16 dpacc = rows_times<D>(Vs, 32 * kt, jl, hl, doop);
-      float ds[16];
+      for (int kt = 0; kt < 2; ++kt) {
+        // S^T and dP^T for keys 32 kt .. 32 kt + 31 (rows) of this lane's query
+        const f32x16 sacc = sw_rows_times<D>(kb, 32 * kt, jl, hl, qop);
+        const f32x16 dpacc = sw_rows_times<D>(vb, 32 * kt, jl, hl, doop);
+        float ds[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const bool ok = (key >> 3) < rv && (key & 7) < cv;
-        const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2)) : 0.f;
-        ds[r] = p * (dpacc[r] - Dq);
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const bool ok = (key >> 3) < rv && (key & 7) < cv;
+          const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2)) : 0.f;
+          ds[r] = p * (dpacc[r] - Dq);
+        }
+        bf16x8 bop[2];
+        to_bop(ds, bop);
+        sw_cols_times<D>(kb, 32 * kt, lane, hl, bop, dqacc);    // dQ^T += K^T dS^T
       }
-      bf16x8 bop[2];
-      to_bop(ds, bop);
-      cols_times<D>(Ks, 32 * kt, lane, hl, bop, dqacc);    // dQ^T += K^T dS^T
     }
+    cur = next;
   }
 
   if (myq >= 0 && (qvalid || g.layout == 1))
@@ -577,7 +680,12 @@ hipError_t launch_dq_t(const Geo& g, bool bf16, const void* q, const void* k, co
                        hipStream_t s) {
   if (bf16) {
     const int64_t chunk = (pair_items(g) + 7) / 8;
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3((unsigned)(8 * chunk * g.bh)), dim3(256), 0, s,
+    const size_t lds = 4 * SwTile<D>::kBytes;
+    auto kern = attn_bwd_dq_kernel<D>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(8 * chunk * g.bh)), dim3(256), lds, s,
                        g, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)o,
                        (const __bf16*)dout, lse, row_ptr, col_idx, scale * kLog2e, scale,
                        (__bf16*)dq, delta);

@@ -30,6 +30,32 @@ __device__ inline void pair_of(const Geo& g, int p, int* a, int* b) {
   *b = 2 * wp + 1 < g.gw ? *a + 1 : -1;
 }
 
+// ---- LDS addressing and direct-to-LDS loads (gfx950) ----
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+
+// 16-byte LDS read at an absolute LDS address
+__device__ inline bf16x8 lds_read16(int addr) { return *(lds_bf16x8*)(uintptr_t)addr; }
+
+// s_waitcnt vmcnt(0), leaving the other counters alone.
+__device__ inline void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Direct-to-LDS load of 16 bytes per lane through a buffer descriptor: lane
+// l reads bytes [soff + voff, +16) of the buffer and writes bytes
+// [16 l, 16 l + 16) of the 1-KB LDS block at dst.  The buffer form keeps the
+// tile address in scalar registers, and (unlike the global form) does not
+// make the compiler drain every outstanding LDS read at each LDS wait.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, char* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)   // gfx950-only builtin: the host pass needs no body
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, soff, 0, 0);
+#endif
+}
+// Raw buffer descriptor over n bytes at p (gfx9 word 3: 32-bit data format).
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
 // Ascending list of one row of a CSR structure (a query block's kept key
 // blocks, or a key block's query blocks in the transposed mask), read through
 // the scalar cache (the constant address space makes these uniform reads
