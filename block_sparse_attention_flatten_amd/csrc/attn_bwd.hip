@@ -12,11 +12,13 @@
 //   * mask transpose: key block c's list of the query blocks that keep it
 //     (bit r of transposed row c = bit c of row r), compacted by nabla_compact;
 //   * dQ: one workgroup per PAIR of query blocks walking the union of their
-//     kept lists (as the forward does); per kept block S^T = K Q^T and
+//     kept lists (as the forward does), K and V tiles by direct-to-LDS loads
+//     into double buffers; per kept block S^T = K Q^T and
 //     dP^T = V dO^T on the matrix cores, dS^T in registers, and
 //     dQ^T += K^T dS^T with K^T operands from transpose loads of the K tile.
 //     It also writes D = rowsum(dO * O) for the second call;
-//   * dK / dV: one workgroup per key block walking its query-block list.
+//   * dK / dV: one workgroup per key block walking its query-block list, Q
+//     and dO tiles (and the block's lse and D) by direct-to-LDS loads.
 //     Wavefronts 0-1 accumulate dV^T += dO^T P, wavefronts 2-3 dK^T += Q^T dS
 //     (both recompute S = Q K^T; the dK side also dP = dO V^T), 32 keys each,
 //     so each lane owns one key and every accumulation stays in registers.
@@ -60,53 +62,11 @@ mask_transpose_kernel(const Geo g, const uint32_t* __restrict__ bits,
 // ---------------------------------------------------------------------------
 template <int D>
 struct BwdShape {
-  // LDS row stride (elements): a stride of 4 (mod 32) banks spreads the 16-byte
-  // row reads of 8 consecutive rows over all banks; the transpose loads of the
-  // same tile then see at most 2-way conflicts.
-  static constexpr int kStride = D + 8;
-  static constexpr int kThreads = 256;
-  static constexpr int kChunks = D / 8;           // 16-byte chunks per token row
-  static constexpr int kRowsPerPass = kThreads / kChunks;
-  static constexpr int kPasses = kN / kRowsPerPass;
   static constexpr int kSteps = D / 16;           // k-steps over d
   static constexpr int kDTiles = D / 32;          // 32-row tiles of a d x 32 accumulator
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
-
-// Two 64 x d bf16 tiles (the same token block of two tensors) staged through
-// registers: fetch() loads the next block while the current one is in use,
-// put() writes the registers to LDS.  Pad rows of latent-edge blocks load row 0
-// of the block (finite data; their weights are forced to 0 by the caller).
-template <int D>
-struct TilePair {
-  using A = BwdShape<D>;
-  u32x4 r0[A::kPasses], r1[A::kPasses];
-  __device__ void fetch(const Geo& g, const __bf16* X0, const __bf16* X1, int64_t hoff,
-                        int row_step, int blk, int tid) {
-    const int chunk = tid % A::kChunks, row = tid / A::kChunks;
-    const BlockCoord bc = block_coord(g, blk);
-    const int rv = block_rows_valid(g, bc), cv = block_cols_valid(g, bc);
-    const int64_t base = hoff + block_base(g, blk, bc) + chunk * 8;
-#pragma unroll
-    for (int p = 0; p < A::kPasses; ++p) {
-      const int r = row + p * A::kRowsPerPass;
-      const bool ok = (r >> 3) < rv && (r & 7) < cv;
-      const int off = ok ? (r >> 3) * row_step + (r & 7) * D : 0;
-      r0[p] = *(const u32x4*)(X0 + base + off);
-      r1[p] = *(const u32x4*)(X1 + base + off);
-    }
-  }
-  __device__ void put(__bf16* T0, __bf16* T1, int tid) const {
-    const int chunk = tid % A::kChunks, row = tid / A::kChunks;
-#pragma unroll
-    for (int p = 0; p < A::kPasses; ++p) {
-      const int r = row + p * A::kRowsPerPass;
-      *(u32x4*)(T0 + r * A::kStride + chunk * 8) = r0[p];
-      *(u32x4*)(T1 + r * A::kStride + chunk * 8) = r1[p];
-    }
-  }
-};
 
 // A lane's token row as matrix-core operand chunks: chunk s holds elements
 // 16 s + 8 hl .. + 7 (zero when the row is not valid).
@@ -118,47 +78,6 @@ __device__ inline void row_operand(const __bf16* X, int64_t off, bool valid, int
     u32x4 raw = {0u, 0u, 0u, 0u};
     if (valid) raw = *(const u32x4*)(X + off + 16 * s + 8 * hl);
     op[s] = __builtin_bit_cast(bf16x8, raw);
-  }
-}
-
-// 32 x 32 product over d: acc[r] = sum_d T[row0 + jl][d] * op[d] with the
-// tile rows as the A operand (16-byte LDS row reads) and op as the B operand.
-template <int D>
-__device__ inline f32x16 rows_times(const __bf16* T, int row0, int jl, int hl,
-                                    const bf16x8 (&op)[D / 16]) {
-  f32x16 acc = {};
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    const bf16x8 a = *(const bf16x8*)(T + (row0 + jl) * BwdShape<D>::kStride + 16 * s + 8 * hl);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, op[s], acc, 0, 0, 0);
-  }
-  return acc;
-}
-
-// acc[dt] += T^T[32 dt + lane % 32][rows] * B over the 32 tile rows
-// row0 .. row0 + 31, as two k-steps.  The A operand comes from the row-major
-// tile through transpose loads: in each 16-lane group, lane i receives element
-// i % 4 of the 4-element rows addressed by lanes 4e + i / 4, so the lane
-// supplying rows k0 + s / 4 and k0 + 8 + s / 4 (k0 = row0 + 16 h + 4 hl),
-// columns 32 dt + (lane & 16) + 4 (s % 4), yields exactly the k order of a
-// B operand built from a 32 x 32 accumulator (see to_bop).
-template <int D>
-__device__ inline void cols_times(const __bf16* T, int row0, int lane, int hl,
-                                  const bf16x8 (&bop)[2], f32x16 (&acc)[D / 32]) {
-  constexpr int St = BwdShape<D>::kStride;
-  const __bf16* src0 = T + ((lane & 15) >> 2) * St + (lane & 16) + 4 * (lane & 3);
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const __bf16* src = src0 + (row0 + 16 * h + 4 * hl) * St + 32 * dt;
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) bf16x4*)(src));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) bf16x4*)(src + 8 * St));
-      const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop[h], acc[dt], 0, 0, 0);
-    }
   }
 }
 
@@ -254,8 +173,13 @@ __device__ inline f32x16 sw_rows_times(int tb, int row0, int jl, int hl,
   return acc;
 }
 
-// acc[dt] += T^T * B over tile rows row0 .. row0 + 31 (see cols_times), the
-// transpose loads addressing the swizzled tile at LDS address tb.
+// acc[dt] += T^T[32 dt + lane % 32][rows] * B over the 32 tile rows
+// row0 .. row0 + 31 of the swizzled tile at LDS address tb, as two k-steps.
+// The A operand comes from transpose loads: in each 16-lane group, lane i
+// receives element i % 4 of the 4-element rows addressed by lanes 4e + i / 4,
+// so the lane supplying rows k0 + s / 4 and k0 + 8 + s / 4 (k0 = row0 + 16 h
+// + 4 hl), columns 32 dt + (lane & 16) + 4 (s % 4), yields exactly the k order
+// of a B operand built from a 32 x 32 accumulator (see to_bop).
 template <int D>
 __device__ inline void sw_cols_times(int tb, int row0, int lane, int hl, const bf16x8 (&bop)[2],
                                      f32x16 (&acc)[D / 32]) {
@@ -401,6 +325,9 @@ attn_bwd_dq_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
 }
 
 // ---- dK and dV ----
+// Q and dO tiles move by direct-to-LDS loads into two buffers each, with the
+// 64 log-sum-exps and D values of the query block beside them; one barrier
+// per step.
 template <int D>
 __global__ void __launch_bounds__(256, 2)
 attn_bwd_dkdv_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
@@ -410,10 +337,9 @@ attn_bwd_dkdv_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
                      float scale_log2, float scale, __bf16* __restrict__ dK,
                      __bf16* __restrict__ dV) {
   using A = BwdShape<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 Qs[kN * A::kStride];
-  __shared__ __attribute__((aligned(16))) __bf16 dOs[kN * A::kStride];
-  __shared__ __attribute__((aligned(16))) float Ls[kN];   // log2-domain lse (+inf: weight 0)
-  __shared__ __attribute__((aligned(16))) float Ds[kN];
+  using T = SwTile<D>;
+  // Q[2], dO[2] tiles, then lse[2][64] and D[2][64] (float)
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int nb = g.nb;
   int64_t head;
@@ -422,12 +348,19 @@ attn_bwd_dkdv_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool dk_side = (wave >> 1) != 0;   // wavefronts 0-1: dV, 2-3: dK
   const int hl = lane >> 5;
   const int jl = lane & 31;
   const int64_t hoff = head * (int64_t)g.head_elems;
   const int row_step = block_row_step(g);
+  const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(Q + hoff, 2u * (uint32_t)g.head_elems);
+  const __amdgpu_buffer_rsrc_t grs = buffer_rsrc(dO + hoff, 2u * (uint32_t)g.head_elems);
+  const uint32_t vec_bytes = 4u * (uint32_t)(nb * kN);
+  const __amdgpu_buffer_rsrc_t lrs = buffer_rsrc(lse + head * nb * kN, vec_bytes);
+  const __amdgpu_buffer_rsrc_t drs = buffer_rsrc(delta + head * nb * kN, vec_bytes);
+  const int lds0 = (int)(uintptr_t)(lds_char*)smem;
+  char* const vec = smem + 4 * T::kBytes;                 // lse[2][64], D[2][64]
 
   // this lane's key row: K (and V on the dK side) as B operands
   const int ks = 32 * (wave & 1) + jl;
@@ -443,44 +376,48 @@ attn_bwd_dkdv_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
   for (int t = 0; t < A::kDTiles; ++t) acc[t] = f32x16{};
 
   KeptList lq = kept_list(col_ptr + head * (nb + 1), row_idx + head * (int64_t)nb * nb, nb, beta);
-  TilePair<D> pre;
-  float lse_n = 0.f, del_n = 0.f;            // threads 0-63: the next block's lse and D
-  auto fetch = [&](int alpha) {
-    pre.fetch(g, Q, dO, hoff, row_step, alpha, tid);
-    if (tid < kN) {
-      const float l = lse[(head * nb + alpha) * kN + tid];
-      lse_n = l > -INFINITY ? l * kLog2e : INFINITY;
-      del_n = delta[(head * nb + alpha) * kN + tid];
+  auto load = [&](int alpha, int buf) {
+    dma_tile<D>(g, qrs, row_step, alpha, wave, lane, smem + buf * T::kBytes);
+    dma_tile<D>(g, grs, row_step, alpha, wave, lane, smem + (2 + buf) * T::kBytes);
+    if (wave == 0) {                 // 64 x 4 bytes each: lane l writes float l
+#if defined(__HIP_DEVICE_COMPILE__)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (lds_void*)(vec + buf * 256), 4, 4u * lane,
+                                               4u * (uint32_t)(alpha * kN), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void*)(vec + 512 + buf * 256), 4,
+                                               4u * lane, 4u * (uint32_t)(alpha * kN), 0, 0);
+#endif
     }
   };
-  if (lq.head != INT_MAX) fetch(lq.head);
-  while (lq.head != INT_MAX) {
+  int cur = lq.head;
+  if (cur != INT_MAX) load(cur, 0);
+  for (int s = 0; cur != INT_MAX; ++s) {
     ++lq.i;
     lq.settle();
-    __syncthreads();
-    pre.put(Qs, dOs, tid);
-    if (tid < kN) {
-      Ls[tid] = lse_n;
-      Ds[tid] = del_n;
-    }
-    __syncthreads();
-    if (lq.head != INT_MAX) fetch(lq.head);
-
+    const int next = lq.head;
+    wait_vmcnt0();                   // this wavefront's loads of cur have landed
+    __syncthreads();                 // ... everyone's, and the other buffers are free
+    if (next != INT_MAX) load(next, (s + 1) & 1);
+    const int qb = lds0 + (s & 1) * T::kBytes;
+    const int gb = lds0 + (2 + (s & 1)) * T::kBytes;
+    const float* Ls = (const float*)(vec + (s & 1) * 256);
+    const float* Ds = (const float*)(vec + 512 + (s & 1) * 256);
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       // S for queries 32 qt .. 32 qt + 31 (rows) and this lane's key (column)
-      const f32x16 sacc = rows_times<D>(Qs, 32 * qt, jl, hl, kop);
+      const f32x16 sacc = sw_rows_times<D>(qb, 32 * qt, jl, hl, kop);
       float x[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const f32x4 l4 = *(const f32x4*)(Ls + 32 * qt + 8 * i + 4 * hl);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)   // a pad key (zero row) keeps weight 0
+        for (int j = 0; j < 4; ++j) {  // pad queries (lse -inf) and pad keys get weight 0
+          const float l2 = l4[j] > -INFINITY ? l4[j] * kLog2e : INFINITY;
           x[4 * i + j] =
-              kvalid ? __builtin_amdgcn_exp2f(fmaf(sacc[4 * i + j], scale_log2, -l4[j])) : 0.f;
+              kvalid ? __builtin_amdgcn_exp2f(fmaf(sacc[4 * i + j], scale_log2, -l2)) : 0.f;
+        }
       }
       if (dk_side) {
-        const f32x16 dpacc = rows_times<D>(dOs, 32 * qt, jl, hl, vop);
+        const f32x16 dpacc = sw_rows_times<D>(gb, 32 * qt, jl, hl, vop);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const f32x4 d4 = *(const f32x4*)(Ds + 32 * qt + 8 * i + 4 * hl);
@@ -489,13 +426,14 @@ attn_bwd_dkdv_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
         }
         bf16x8 bop[2];
         to_bop(x, bop);
-        cols_times<D>(Qs, 32 * qt, lane, hl, bop, acc);     // dK^T += Q^T dS
+        sw_cols_times<D>(qb, 32 * qt, lane, hl, bop, acc);     // dK^T += Q^T dS
       } else {
         bf16x8 bop[2];
         to_bop(x, bop);
-        cols_times<D>(dOs, 32 * qt, lane, hl, bop, acc);    // dV^T += dO^T P
+        sw_cols_times<D>(gb, 32 * qt, lane, hl, bop, acc);     // dV^T += dO^T P
       }
     }
+    cur = next;
   }
 
   if (kvalid || g.layout == 1) {
@@ -709,10 +647,15 @@ hipError_t launch_dkdv_t(const Geo& g, bool bf16, const void* q, const void* k, 
                          void* dv, hipStream_t s) {
   if (bf16) {
     const int64_t chunk = (g.nb + 7) / 8;
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)(8 * chunk * g.bh)), dim3(256), 0,
-                       s, g, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                       (const __bf16*)dout, lse, delta, col_ptr, row_idx, scale * kLog2e, scale,
-                       (__bf16*)dk, (__bf16*)dv);
+    const size_t lds = 4 * SwTile<D>::kBytes + 4 * 256;
+    auto kern = attn_bwd_dkdv_kernel<D>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(8 * chunk * g.bh)), dim3(256), lds, s, g,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout,
+                       lse, delta, col_ptr, row_idx, scale * kLog2e, scale, (__bf16*)dk,
+                       (__bf16*)dv);
     return hipGetLastError();
   }
   const size_t lds = (2 * kN * D + 2 * kN) * sizeof(float);
