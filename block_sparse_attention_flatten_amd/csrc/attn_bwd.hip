@@ -19,10 +19,13 @@
 //     It also writes D = rowsum(dO * O) for the second call;
 //   * dK / dV: one workgroup per key block walking its query-block list, Q
 //     and dO tiles (and the block's lse and D) by direct-to-LDS loads.
-//     Wavefronts 0-1 accumulate dV^T += dO^T P, wavefronts 2-3 dK^T += Q^T dS
-//     (both recompute S = Q K^T; the dK side also dP = dO V^T), 32 keys each,
-//     so each lane owns one key and every accumulation stays in registers.
+//     Wavefronts 0-1 compute S = Q K^T and P and accumulate dV^T += dO^T P;
+//     they hand P to wavefronts 2-3, which compute dP = dO V^T and
+//     accumulate dK^T += Q^T dS.  32 keys per wavefront, so each lane owns
+//     one key and every accumulation stays in registers; S is computed once.
 // float32 inputs use plain per-thread kernels of the same structure.
+#include <type_traits>
+
 #include "attn_common.hpp"
 
 namespace nabla {
@@ -83,13 +86,8 @@ __device__ inline void row_operand(const __bf16* X, int64_t off, bool valid, int
 
 // Accumulator element r of a 32 x 32 tile sits in row 8 (r / 4) + 4 hl + r % 4
 // of this lane's column; as a B operand over those 32 rows, k-step h takes
-// elements 8 h .. 8 h + 7.
-__device__ inline void to_bop(const float (&x)[16], bf16x8 (&bop)[2]) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) bop[h][e] = (__bf16)x[8 * h + e];
-}
+// elements 8 h .. 8 h + 7 (element e of operand h is accumulator element
+// 8 h + e).
 
 // store a lane's d-vector held as accumulator columns: element r of tile dt is
 // component 32 dt + 8 (r / 4) + 4 hl + r % 4
@@ -154,52 +152,63 @@ __device__ inline void dma_tile(const Geo& g, __amdgpu_buffer_rsrc_t rs, int row
     int r, c;
     T::op_rc(o, lane, &r, &c);
     const bool ok = (r >> 3) < rv && (r & 7) < cv;
-    const int el = (ok ? (r >> 3) * row_step + (r & 7) * D : 0) + c * 8;
-    dma16(rs, 2u * (uint32_t)el, sb, dst + T::op_dst(o));
+    // a head holds at most 2^26 bytes, so 2^31 is out of range even with sb added
+    const uint32_t voff = ok ? 2u * (uint32_t)((r >> 3) * row_step + (r & 7) * D + c * 8)
+                             : 0x80000000u;
+    dma16(rs, voff, sb, dst + T::op_dst(o));
   }
 }
 
-// 32 x 32 product over d with tile rows row0 + jl as the A operand (16-byte
-// row reads of a swizzled tile at LDS address tb) and op as the B operand.
+// A operand of a 32 x 32 x 16 product over d: tile row `row` of the swizzled
+// tile at LDS address tb, k-step st (elements 16 st + 8 hl .. + 7), by one
+// 16-byte read.
 template <int D>
-__device__ inline f32x16 sw_rows_times(int tb, int row0, int jl, int hl,
-                                       const bf16x8 (&op)[D / 16]) {
-  f32x16 acc = {};
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    const bf16x8 a = lds_read16(tb + SwTile<D>::addr(row0 + jl, 2 * s + hl));
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, op[s], acc, 0, 0, 0);
-  }
-  return acc;
+__device__ inline bf16x8 sw_row_read(int tb, int row, int st, int hl) {
+  return lds_read16(tb + SwTile<D>::addr(row, 2 * st + hl));
 }
 
-// acc[dt] += T^T[32 dt + lane % 32][rows] * B over the 32 tile rows
-// row0 .. row0 + 31 of the swizzled tile at LDS address tb, as two k-steps.
-// The A operand comes from transpose loads: in each 16-lane group, lane i
-// receives element i % 4 of the 4-element rows addressed by lanes 4e + i / 4,
-// so the lane supplying rows k0 + s / 4 and k0 + 8 + s / 4 (k0 = row0 + 16 h
-// + 4 hl), columns 32 dt + (lane & 16) + 4 (s % 4), yields exactly the k order
-// of a B operand built from a 32 x 32 accumulator (see to_bop).
+// A operand of acc[dt] += X^T[32 dt + lane % 32][rows] * B over the 16 tile
+// rows row0 + 16 h .. + 15 of the swizzled tile at LDS address tb (the
+// product over tile rows, X^T from transpose loads).  In each 16-lane group,
+// lane i receives element i % 4 of the 4-element rows addressed by lanes
+// 4e + i / 4, so the lane supplying rows k0 + s / 4 and k0 + 8 + s / 4
+// (k0 = row0 + 16 h + 4 hl), columns 32 dt + (lane & 16) + 4 (s % 4), yields
+// exactly the k order of a B operand built from a 32 x 32 accumulator.
 template <int D>
-__device__ inline void sw_cols_times(int tb, int row0, int lane, int hl, const bf16x8 (&bop)[2],
-                                     f32x16 (&acc)[D / 32]) {
+__device__ inline bf16x8 sw_tr_read(int tb, int row0, int h, int dt, int lane) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-  const int rsub = (lane & 15) >> 2;
-  const int csub = (lane & 16) + 4 * (lane & 3);
+  const int col = 32 * dt + (lane & 16) + 4 * (lane & 3);
+  const int r = row0 + 16 * h + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int c = (col & 7) * 2;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)(uintptr_t)(tb + SwTile<D>::addr(r, col >> 3) + c));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)(uintptr_t)(tb + SwTile<D>::addr(r + 8, col >> 3) + c));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// N matrix instructions in a fixed order, the A operand of slot i read
+// kAhead slots earlier so that LDS latency overlaps the matrix work:
+// read(j) returns slot j's A operand, mma(i, a) issues slot i's instruction,
+// work(i) is the vector work placed beside it.  The scheduling barrier keeps
+// each slot's content together.
+template <int N, typename Read, typename Mma, typename Work>
+__device__ inline void run_slots(Read read, Mma mma, Work work) {
+  constexpr int kAhead = N < 3 ? N : 3;
+  bf16x8 a[N];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    const int col = 32 * dt + csub;
+  for (int j = 0; j < kAhead; ++j) a[j] = read(j);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = row0 + 16 * h + 4 * hl + rsub;
-      const int lo_a = tb + SwTile<D>::addr(r, col >> 3) + (col & 7) * 2;
-      const int hi_a = tb + SwTile<D>::addr(r + 8, col >> 3) + (col & 7) * 2;
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)lo_a);
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)hi_a);
-      const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop[h], acc[dt], 0, 0, 0);
-    }
+  for (int i = 0; i < N; ++i) {
+    mma(i, a[i]);
+    work(i);
+    if (i + kAhead < N) a[i + kAhead] = read(i + kAhead);
+    __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+__device__ inline f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // ---- dQ (and D) ----
@@ -296,26 +305,69 @@ attn_bwd_dq_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
     if (grp == 0 ? in_a : in_b) {    // wavefront-uniform: a kept block of ours
       const int kb = lds0 + (s & 1) * T::kBytes;
       const int vb = lds0 + (2 + (s & 1)) * T::kBytes;
-      const BlockCoord bc = block_coord(g, cur);
-      const int rv = block_rows_valid(g, bc);
-      const int cv = block_cols_valid(g, bc);
+      // One run of 4 kSteps + 4 kDTiles matrix instructions, for keys
+      // 32 kt .. 32 kt + 31 (kt = 0, 1) of the block and this lane's query:
+      //   S^T(0) = K Q^T, dP^T(0) = V dO^T, S^T(1), dP^T(1)   (tile rows),
+      //   dQ^T += K^T dS^T for kt = 0, then 1                 (transpose loads),
+      // with the vector work of one stage beside the next one's products:
+      // p = exp2(S scale log2(e) - lse log2(e)) of half kt beside dP^T(kt),
+      // dS^T(0) = P (dP - D) beside S^T(1), dS^T(1) beside the kt = 0 dQ
+      // products.
+      constexpr int kR = A::kSteps;                  // slots per row product
+      constexpr int kQ = 2 * A::kDTiles;             // dQ slots per half
+      f32x16 sacc[2], dpacc[2];
+      bf16x8 b[2][2];                                // dS^T as B operands
+      // Pad keys (zero rows of the K and V tiles) need no mask: S = dP = 0
+      // there, and K^T's zero rows drop their dS from dQ.  Their p =
+      // exp2(-lse log2(e)) is clamped to 2^64 so that dS stays finite (real
+      // keys have S scale log2(e) - lse log2(e) <= 0, untouched by the clamp).
+      auto exps = [&](int kt, int r) {
+        sacc[kt][r] =
+            __builtin_amdgcn_exp2f(fminf(fmaf(sacc[kt][r], scale_log2, -lse2), 64.0f));
+      };
+      auto ds = [&](int kt, int r) {
+        b[kt][r >> 3][r & 7] = (__bf16)(sacc[kt][r] * (dpacc[kt][r] - Dq));
+      };
+      run_slots<4 * kR + 2 * kQ>(
+          [&](int j) {
+            if (j < 4 * kR) {
+              const int part = j / kR;               // S(0), dP(0), S(1), dP(1)
+              return sw_row_read<D>((part & 1) ? vb : kb, 32 * (part >> 1) + jl, j % kR, hl);
+            }
+            const int jj = j - 4 * kR;
+            return sw_tr_read<D>(kb, 32 * (jj / kQ), (jj / A::kDTiles) & 1, jj % A::kDTiles,
+                                 lane);
+          },
+          [&](int i, bf16x8 a) {
+            if (i < 4 * kR) {
+              const int part = i / kR, st = i % kR, kt = part >> 1;
+              if (part & 1)
+                dpacc[kt] = mfma_bf16(a, doop[st], st == 0 ? f32x16{} : dpacc[kt]);
+              else
+                sacc[kt] = mfma_bf16(a, qop[st], st == 0 ? f32x16{} : sacc[kt]);
+            } else {
+              const int jj = i - 4 * kR;
+              const int dt = jj % A::kDTiles;
+              dqacc[dt] = mfma_bf16(a, b[jj / kQ][(jj / A::kDTiles) & 1], dqacc[dt]);
+            }
+          },
+          [&](int i) {
+            constexpr int kPer = 16 / kR;            // elements per row-product slot
+            if (i < 4 * kR) {
+              const int part = i / kR, st = i % kR;
+              if (part == 1 || part == 3) {          // beside dP(kt): exponentials of half kt
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        // S^T and dP^T for keys 32 kt .. 32 kt + 31 (rows) of this lane's query
-        const f32x16 sacc = sw_rows_times<D>(kb, 32 * kt, jl, hl, qop);
-        const f32x16 dpacc = sw_rows_times<D>(vb, 32 * kt, jl, hl, doop);
-        float ds[16];
+                for (int e = 0; e < kPer; ++e) exps(part >> 1, st * kPer + e);
+              } else if (part == 2) {                // beside S(1): dS(0)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
-          const bool ok = (key >> 3) < rv && (key & 7) < cv;
-          const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2)) : 0.f;
-          ds[r] = p * (dpacc[r] - Dq);
-        }
-        bf16x8 bop[2];
-        to_bop(ds, bop);
-        sw_cols_times<D>(kb, 32 * kt, lane, hl, bop, dqacc);    // dQ^T += K^T dS^T
-      }
+                for (int e = 0; e < kPer; ++e) ds(0, st * kPer + e);
+              }
+            } else if (i - 4 * kR < kQ) {            // beside the first dQ half: dS(1)
+              constexpr int kPerQ = 16 / kQ;
+#pragma unroll
+              for (int e = 0; e < kPerQ; ++e) ds(1, (i - 4 * kR) * kPerQ + e);
+            }
+          });
     }
     cur = next;
   }
@@ -326,8 +378,12 @@ attn_bwd_dq_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
 
 // ---- dK and dV ----
 // Q and dO tiles move by direct-to-LDS loads into two buffers each, with the
-// 64 log-sum-exps and D values of the query block beside them; one barrier
-// per step.
+// 64 log-sum-exps and D values of the query block beside them.  Two barriers
+// per step: after the first, the dV side computes S and P and hands P (bf16)
+// to the dK side through LDS while the dK side computes dP; after the second,
+// the dV side accumulates dV^T += dO^T P and the dK side dK^T += Q^T dS with
+// dS = P (dP - D).  Every wavefront issues 4 x 8 matrix instructions per step,
+// with its LDS operand reads issued several instructions ahead.
 template <int D>
 __global__ void __launch_bounds__(256, 2)
 attn_bwd_dkdv_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
@@ -338,7 +394,7 @@ attn_bwd_dkdv_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
                      __bf16* __restrict__ dV) {
   using A = BwdShape<D>;
   using T = SwTile<D>;
-  // Q[2], dO[2] tiles, then lse[2][64] and D[2][64] (float)
+  // Q[2], dO[2] tiles, lse[2][64] and D[2][64] (float), then P (8 KB)
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int nb = g.nb;
@@ -361,24 +417,29 @@ attn_bwd_dkdv_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
   const __amdgpu_buffer_rsrc_t drs = buffer_rsrc(delta + head * nb * kN, vec_bytes);
   const int lds0 = (int)(uintptr_t)(lds_char*)smem;
   char* const vec = smem + 4 * T::kBytes;                 // lse[2][64], D[2][64]
+  // P of a step, bf16, in the B-operand order of the dV side: [key half][qt][h]
+  // blocks of 1 KB, 16 bytes per lane; the dK lane with the same key reads it
+  char* const pbuf = vec + 1024;
+  const int pslot = (wave & 1) * 4096 + lane * 16;
 
-  // this lane's key row: K (and V on the dK side) as B operands
+  // this lane's key row: K on the dV side (S = Q K^T), V on the dK side
+  // (dP = dO V^T), as B operands
   const int ks = 32 * (wave & 1) + jl;
   const BlockCoord kc = block_coord(g, beta);
   const bool kvalid = (ks >> 3) < block_rows_valid(g, kc) && (ks & 7) < block_cols_valid(g, kc);
   const int64_t koff = hoff + block_base(g, beta, kc) + (ks >> 3) * row_step + (ks & 7) * D;
-  bf16x8 kop[A::kSteps], vop[A::kSteps];
-  row_operand<D>(K, koff, kvalid, hl, kop);
-  row_operand<D>(V, koff, kvalid && dk_side, hl, vop);
-
+  bf16x8 rop[A::kSteps];
+  row_operand<D>(dk_side ? V : K, koff, kvalid, hl, rop);
   f32x16 acc[A::kDTiles];
 #pragma unroll
   for (int t = 0; t < A::kDTiles; ++t) acc[t] = f32x16{};
 
   KeptList lq = kept_list(col_ptr + head * (nb + 1), row_idx + head * (int64_t)nb * nb, nb, beta);
+  // wavefront 0 moves the lse and D vectors first, so that it can wait for
+  // them alone (vmcnt counts its loads in order) and rewrite the lse in place
+  // as exp2-domain offsets: lse * log2(e), +inf for pad queries (weight 0)
+  constexpr int kTileOps = 2 * (T::kOps / 4);            // per wavefront and step
   auto load = [&](int alpha, int buf) {
-    dma_tile<D>(g, qrs, row_step, alpha, wave, lane, smem + buf * T::kBytes);
-    dma_tile<D>(g, grs, row_step, alpha, wave, lane, smem + (2 + buf) * T::kBytes);
     if (wave == 0) {                 // 64 x 4 bytes each: lane l writes float l
 #if defined(__HIP_DEVICE_COMPILE__)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (lds_void*)(vec + buf * 256), 4, 4u * lane,
@@ -387,58 +448,166 @@ attn_bwd_dkdv_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
                                                4u * lane, 4u * (uint32_t)(alpha * kN), 0, 0);
 #endif
     }
+    dma_tile<D>(g, qrs, row_step, alpha, wave, lane, smem + buf * T::kBytes);
+    dma_tile<D>(g, grs, row_step, alpha, wave, lane, smem + (2 + buf) * T::kBytes);
   };
-  int cur = lq.head;
-  if (cur != INT_MAX) load(cur, 0);
-  for (int s = 0; cur != INT_MAX; ++s) {
-    ++lq.i;
-    lq.settle();
-    const int next = lq.head;
-    wait_vmcnt0();                   // this wavefront's loads of cur have landed
-    __syncthreads();                 // ... everyone's, and the other buffers are free
-    if (next != INT_MAX) load(next, (s + 1) & 1);
-    const int qb = lds0 + (s & 1) * T::kBytes;
-    const int gb = lds0 + (2 + (s & 1)) * T::kBytes;
-    const float* Ls = (const float*)(vec + (s & 1) * 256);
-    const float* Ds = (const float*)(vec + 512 + (s & 1) * 256);
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      // S for queries 32 qt .. 32 qt + 31 (rows) and this lane's key (column)
-      const f32x16 sacc = sw_rows_times<D>(qb, 32 * qt, jl, hl, kop);
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 l4 = *(const f32x4*)(Ls + 32 * qt + 8 * i + 4 * hl);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {  // pad queries (lse -inf) and pad keys get weight 0
-          const float l2 = l4[j] > -INFINITY ? l4[j] * kLog2e : INFINITY;
-          x[4 * i + j] =
-              kvalid ? __builtin_amdgcn_exp2f(fmaf(sacc[4 * i + j], scale_log2, -l2)) : 0.f;
-        }
-      }
-      if (dk_side) {
-        const f32x16 dpacc = sw_rows_times<D>(gb, 32 * qt, jl, hl, vop);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 d4 = *(const f32x4*)(Ds + 32 * qt + 8 * i + 4 * hl);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) x[4 * i + j] *= dpacc[4 * i + j] - d4[j];
-        }
-        bf16x8 bop[2];
-        to_bop(x, bop);
-        sw_cols_times<D>(qb, 32 * qt, lane, hl, bop, acc);     // dK^T += Q^T dS
-      } else {
-        bf16x8 bop[2];
-        to_bop(x, bop);
-        sw_cols_times<D>(gb, 32 * qt, lane, hl, bop, acc);     // dV^T += dO^T P
+  auto lse_to_exp2 = [&](int buf) {  // wavefront 0, after its vector loads landed
+    float* l = (float*)(vec + buf * 256);
+    const float v = l[lane];
+    l[lane] = v > -INFINITY ? v * kLog2e : INFINITY;
+  };
+
+  // Barrier for LDS data only: waits for this wavefront's LDS accesses, not
+  // for its direct-to-LDS loads of the next step (which a fence, and hence
+  // __syncthreads, would also wait for).  The clobber keeps the compiler from
+  // moving memory accesses across it.
+  auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  // 2 kSteps slots: the 32 x 32 products over d for queries 32 qt .. +31,
+  // qt = 0 then 1 (accumulation chains issue back to back), A operands from
+  // the rows of the tile at tb, B = this lane's key row
+  auto rows_slots = [&](int tb, f32x16 (&out)[2], auto work) {
+    run_slots<2 * A::kSteps>(
+        [&](int j) { return sw_row_read<D>(tb, 32 * (j / A::kSteps) + jl, j % A::kSteps, hl); },
+        [&](int i, bf16x8 a) {
+          const int qt = i / A::kSteps, st = i % A::kSteps;
+          out[qt] = mfma_bf16(a, rop[st], st == 0 ? f32x16{} : out[qt]);
+        },
+        work);
+  };
+  // 4 kDTiles slots: acc[dt] += X^T(d rows 32 dt.., queries 32 qt + 16 h ..) b[qt][h]
+  auto cols_slots = [&](int tb, const bf16x8 (&b)[2][2], auto work) {
+    run_slots<4 * A::kDTiles>(
+        [&](int j) {
+          return sw_tr_read<D>(tb, 32 * (j / (2 * A::kDTiles)), (j / A::kDTiles) & 1,
+                               j % A::kDTiles, lane);
+        },
+        [&](int i, bf16x8 a) {
+          const int qt = i / (2 * A::kDTiles), h = (i / A::kDTiles) & 1, dt = i % A::kDTiles;
+          acc[dt] = mfma_bf16(a, b[qt][h], acc[dt]);
+        },
+        work);
+  };
+
+  // the two roles run separate copies of the loop (the same barriers in the
+  // same order), so that each copy's registers are allocated on their own
+  auto walk = [&](auto role) {
+    constexpr bool kDK = decltype(role)::value;
+    int cur = lq.head;
+    if (cur != INT_MAX) {
+      load(cur, 0);
+      if (wave == 0) {
+        __builtin_amdgcn_s_waitcnt(0x0F70 | kTileOps);   // vmcnt(kTileOps): lse, D landed
+        lse_to_exp2(0);
       }
     }
-    cur = next;
-  }
+    for (int s = 0; cur != INT_MAX; ++s) {
+      ++lq.i;
+      lq.settle();
+      const int next = lq.head;
+      wait_vmcnt0();                 // this wavefront's loads of cur have landed
+      __syncthreads();               // ... everyone's, and the other buffers are free
+      if (next != INT_MAX) load(next, (s + 1) & 1);
+      const int qb = lds0 + (s & 1) * T::kBytes;
+      const int gb = lds0 + (2 + (s & 1)) * T::kBytes;
+      const float* Ls = (const float*)(vec + (s & 1) * 256);
+      const float* Ds = (const float*)(vec + 512 + (s & 1) * 256);
+      bf16x8 b[2][2];                // dV side: P; dK side: dS
+      if constexpr (!kDK) {
+        // phase 1: S, then p = exp2(S scale log2(e) - lse log2(e)); the
+        // weights of queries 0-31 are computed in the slots of queries 32-63.
+        // Pad keys need no mask: a key's weights only reach its own column
+        // of the results, which is never stored.
+        f32x16 sacc[2];
+        f32x4 l4[2][4];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) l4[qt][i] = *(const f32x4*)(Ls + 32 * qt + 8 * i + 4 * hl);
+        auto weights = [&](int qt, int e) {   // elements e, e + 1 of S(qt)
+          const float x0 = __builtin_amdgcn_exp2f(
+              fmaf(sacc[qt][e], scale_log2, -l4[qt][e >> 2][e & 3]));
+          const float x1 = __builtin_amdgcn_exp2f(
+              fmaf(sacc[qt][e + 1], scale_log2, -l4[qt][e >> 2][(e & 3) + 1]));
+          b[qt][e >> 3][e & 7] = (__bf16)x0;
+          b[qt][e >> 3][(e & 7) + 1] = (__bf16)x1;
+        };
+        rows_slots(qb, sacc, [&](int i) {
+          if (i >= A::kSteps) {
+            constexpr int kPer = 16 / A::kSteps;   // elements per slot
+#pragma unroll
+            for (int e = 0; e < kPer; e += 2) weights(0, (i - A::kSteps) * kPer + e);
+          }
+        });
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) weights(1, e);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) *(bf16x8*)(pbuf + pslot + (2 * qt + h) * 1024) = b[qt][h];
+        lds_barrier();               // P of this step is in LDS
+        // phase 2: dV^T += dO^T P
+        cols_slots(gb, b, [&](int) {});
+        if (wave == 0 && next != INT_MAX) {
+          __builtin_amdgcn_s_waitcnt(0x0F70 | kTileOps);
+          lse_to_exp2((s + 1) & 1);
+        }
+      } else {
+        // phase 1: dP - D, the rows of queries 0-31 in the slots of 32-63
+        f32x16 dpacc[2];
+        f32x4 d4[2][4];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d4[qt][i] = *(const f32x4*)(Ds + 32 * qt + 8 * i + 4 * hl);
+        float dpm[2][16];
+        rows_slots(gb, dpacc, [&](int i) {
+          if (i >= A::kSteps) {
+            constexpr int kPer = 16 / A::kSteps;
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) {
+              const int el = (i - A::kSteps) * kPer + e;
+              dpm[0][el] = dpacc[0][el] - d4[0][el >> 2][el & 3];
+            }
+          }
+        });
+#pragma unroll
+        for (int el = 0; el < 16; ++el) dpm[1][el] = dpacc[1][el] - d4[1][el >> 2][el & 3];
+        lds_barrier();               // P of this step is in LDS
+        // phase 2: dS = P (dP - D); dK^T += Q^T dS.  dS of queries 32-63 is
+        // formed in the slots of 0-31.
+        bf16x8 p8[2][2];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) p8[qt][h] = *(const bf16x8*)(pbuf + pslot + (2 * qt + h) * 1024);
+        auto ds = [&](int qt, int e) {
+          b[qt][e >> 3][e & 7] = (__bf16)((float)p8[qt][e >> 3][e & 7] * dpm[qt][e]);
+        };
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ds(0, e);
+        cols_slots(qb, b, [&](int i) {
+          constexpr int kHalf = 2 * A::kDTiles;      // slots of queries 0-31
+          if (i < kHalf) {
+            constexpr int kPer = 16 / kHalf;
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) ds(1, i * kPer + e);
+          }
+        });
+      }
+      cur = next;
+    }
+  };
+  if (dk_side) walk(std::true_type{});
+  else walk(std::false_type{});
 
   if (kvalid || g.layout == 1) {
     __bf16* dst = (dk_side ? dK : dV) + koff;
-    store_row<D>(dst, acc, kvalid ? (dk_side ? scale : 1.0f) : 0.f, hl);
+    if (!kvalid) {                   // pad key of the blocked layout: zeros
+#pragma unroll
+      for (int t = 0; t < A::kDTiles; ++t) acc[t] = f32x16{};
+    }
+    store_row<D>(dst, acc, dk_side ? scale : 1.0f, hl);
   }
 }
 
@@ -647,7 +816,7 @@ hipError_t launch_dkdv_t(const Geo& g, bool bf16, const void* q, const void* k, 
                          void* dv, hipStream_t s) {
   if (bf16) {
     const int64_t chunk = (g.nb + 7) / 8;
-    const size_t lds = 4 * SwTile<D>::kBytes + 4 * 256;
+    const size_t lds = 4 * SwTile<D>::kBytes + 4 * 256 + 8192;
     auto kern = attn_bwd_dkdv_kernel<D>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
