@@ -59,6 +59,8 @@ def parse():
                     help="skip the dense reference (the same kernel with every block kept)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the achievable matrix-core / copy rate measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 2 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -76,6 +78,68 @@ def copy_calibration():
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
+
+
+def achievable_peaks(torch, stream, ev):
+    """What this GPU sustains right now, for reading the roofline fractions:
+    back-to-back bf16 matrix instructions on every CU (probe/peaks.hip, its own
+    library) and a plain 2 GiB device copy.  None if the probe library is not
+    built."""
+    import ctypes
+    path = os.path.join(ROOT, "block_sparse_attention_flatten_amd", "libnabla_probe.so")
+    if not os.path.exists(path):
+        log("achievable peaks skipped: libnabla_probe.so not built")
+        return None
+    lib = ctypes.CDLL(path)
+    lib.nabla_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    lib.nabla_probe_mfma_bf16.restype = ctypes.c_int
+    lib.nabla_probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.nabla_probe_mfma_bf16_flops.restype = ctypes.c_double
+    grid, iters = 256 * 3, 40000        # 3 workgroups per CU: all resident at once
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+
+    def probe():
+        st = lib.nabla_probe_mfma_bf16(grid, iters, ctypes.c_void_p(out.data_ptr()),
+                                       ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"mfma probe launch failed ({st})")
+
+    def timed(fn, reps):
+        fn()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    mfma_ms = timed(probe, 3)
+    lib.nabla_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_int, ctypes.c_void_p]
+    lib.nabla_probe_copy.restype = ctypes.c_int
+    n = 1 << 29                         # 2 GiB of float32 each way
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+
+    def copy():
+        st = lib.nabla_probe_copy(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                  4 * n, 256 * 32, ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"copy probe launch failed ({st})")
+
+    copy_ms = timed(copy, 3)
+    torch_copy_ms = timed(lambda: y.copy_(x), 3)
+    del x, y, out
+    return {
+        "mfma_bf16_tflops": round(lib.nabla_probe_mfma_bf16_flops(grid, iters)
+                                  / (mfma_ms * 1e-3) / 1e12, 1),
+        "hbm_copy_gbs": round(2 * 4 * n / (copy_ms * 1e-3) / 1e9, 1),
+        "torch_copy_gbs": round(2 * 4 * n / (torch_copy_ms * 1e-3) / 1e9, 1),
+        "how": "back-to-back v_mfma_f32_32x32x16_bf16 on all CUs; streaming 2 GiB device copy "
+               "(probe/peaks.hip) and torch's copy_, read + write bytes",
+    }
 
 
 KERNEL_SOURCES = ("attn_fwd_vt.hip", "attn_common.hpp", "nabla_common.hpp")
@@ -263,6 +327,10 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (mask {mask_avg:.3f}, "
         f"attn {attn_avg:.3f})")
 
+    achievable = None if args.no_peaks else achievable_peaks(torch, stream, ev)
+    if achievable is not None:
+        log(f"achievable peaks: {achievable}")
+
     # per-stage breakdown (separate, untimed-region runs) and the explicit reorder
     def time_call(fn, reps=5):
         a, b = ev(), ev()
@@ -344,6 +412,7 @@ def main():
             "unit": "GB/s",
             "frac": round(mc_bytes / (mc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         },
+        "achievable_peaks": achievable,
         "stages_ms": {k_: round(v_, 4) for k_, v_ in stages.items()},
         "attn_ms_min_median": [round(attn_ms[0], 4), round(attn_ms[len(attn_ms) // 2], 4)],
         "sparsity": round(sparsity, 4),

@@ -14,6 +14,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libnabla.so")
+PROBE_LIB = os.path.join(PKG, "libnabla_probe.so")
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for all device code (hipcc would
@@ -71,7 +72,17 @@ def build_library(out: str = LIB, verbose: bool = False) -> str:
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in jobs]],
          verbose)
     os.replace(tmp, out)
+    build_probe(verbose)
     return out
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The benchmark's matrix-core rate probe (probe/peaks.hip) as its own library."""
+    src = os.path.join(PKG, "probe", "peaks.hip")
+    tmp = PROBE_LIB + ".tmp"
+    _run([hipcc(), *HIP_FLAGS, "-shared", "-o", tmp, src], verbose)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

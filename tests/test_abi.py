@@ -144,3 +144,26 @@ def test_status_strings():
     for code in _lib.STATUS:
         assert lib.nabla_status_string(code).decode() != "unknown status"
     assert lib.nabla_status_string(12345).decode() == "unknown status"
+
+
+def test_probe_library_exports():
+    """The benchmark's rate probe (probe/peaks.hip) is built beside libnabla and
+    exports its three calls; only bench.py loads it."""
+    path = os.path.join(os.path.dirname(_lib.LIB_PATH), "libnabla_probe.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT\s+(nabla_probe_\w+)", out))
+    assert exported == {"nabla_probe_mfma_bf16", "nabla_probe_mfma_bf16_flops",
+                        "nabla_probe_copy"}
+    lib = ctypes.CDLL(path)
+    lib.nabla_probe_mfma_bf16_flops.restype = ctypes.c_double
+    lib.nabla_probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    assert lib.nabla_probe_mfma_bf16_flops(2, 3) == 2 * 4 * 3 * 4 * 2 * 32 * 32 * 16
+    # argument checks fail before any launch (no GPU touched)
+    lib.nabla_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_int, ctypes.c_void_p]
+    assert lib.nabla_probe_copy(None, FAKE, 16, 1, None) == -1
+    assert lib.nabla_probe_copy(FAKE, FAKE, 15, 1, None) == -1
+    lib.nabla_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    assert lib.nabla_probe_mfma_bf16(0, 1, FAKE, None) == -1
