@@ -142,6 +142,33 @@ def achievable_peaks(torch, stream, ev):
     }
 
 
+def torch_flash_reference(torch, cfg, q, k, v, time_call, attn_ms):
+    """torch's flash-attention backend (no mask, all valid tokens) on the same
+    Q, K, V as a tuned dense kernel of this box.  Only the flash backend is
+    allowed: the math backend would materialise the S x S scores.  None when
+    it is unavailable or the inputs are not bf16."""
+    if cfg.torch_dtype != torch.bfloat16:
+        return None
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    B, h, d = cfg.batch, cfg.heads, cfg.head_dim
+    S = cfg.T * cfg.H * cfg.W                    # THW tensors hold valid tokens only
+    qs, ks, vs = (x.reshape(B, h, S, d) for x in (q, k, v))
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            ms = time_call(lambda: torch.nn.functional.scaled_dot_product_attention(qs, ks, vs),
+                           reps=3)
+    except RuntimeError as e:
+        log(f"torch flash reference unavailable: {e}")
+        return None
+    flops = 4 * S * S * d * B * h
+    out = {"what": "torch scaled_dot_product_attention, flash backend, full attention over "
+                   "the valid tokens", "ms": round(ms, 3),
+           "tflops_valid_tokens": round(flops / (ms * 1e-3) / 1e12, 1),
+           "speedup_sparse_vs_torch_flash": round(ms / attn_ms, 3)}
+    log(f"torch flash reference: {out}")
+    return out
+
+
 KERNEL_SOURCES = ("attn_fwd_vt.hip", "attn_common.hpp", "nabla_common.hpp")
 
 
@@ -500,6 +527,8 @@ def main():
         }
         log(f"dense reference: {dense_ms:.2f} ms ({result['dense_reference']['tflops']} TFLOP/s)")
         del rp_full, ci_full
+        result["dense_reference"]["torch_sdpa_flash"] = torch_flash_reference(
+            torch, cfg, q, k, v, time_call, attn_avg)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, thr, sta, args.cpu_seconds)
