@@ -83,16 +83,15 @@ def test_max_blocks():
     _run(cfg, q, k, v, label="max_blocks")
 
 
-def test_backward_720p_sampled():
-    """Gradients at the 720p bench shape (all 40 heads on the GPU, the forward
-    through nabla_attn_fwd_vt_lse): one sampled head's mask checked in full,
-    dq and lse of sampled query blocks, dk and dv of sampled key blocks (the
-    oracle over every query block that keeps them)."""
+def _backward_sampled(cfg, n_rows, n_cols, label):
+    """Gradients in the bench's launch configuration (every head on the GPU,
+    the forward through nabla_attn_fwd_vt_lse): one sampled head's mask checked
+    in full, dq and lse of sampled query blocks, dk and dv of sampled key
+    blocks (the oracle over every query block that keeps them)."""
     import math
     import block_sparse_attention_flatten_amd as nabla
     from gpu_helpers import geom_of
-    cfg = synth.config("720p")
-    log(f"720p backward: generating inputs {cfg}")
+    log(f"{label}: generating inputs {cfg}")
     q, k, v = synth.make_qkv(cfg, device="cuda")
     dout = synth.make_tensor(cfg, 3, device="cuda")
     res = run_pipeline(cfg, q, k, v, out_dtype=torch.bfloat16)
@@ -105,7 +104,7 @@ def test_backward_720p_sampled():
     nabla.nabla_attn_fwd_vt_lse(g, q, k, vt, res["rp"], res["ci"], scale, o, lse)
     bw = nabla.backward(g, q, k, v, o, lse, dout, res["bits"], res["rp"], res["ci"], scale)
     torch.cuda.synchronize()
-    log("720p backward: GPU done")
+    log(f"{label}: GPU done")
     og = ogeom(cfg)
     nb = g.nb
     h = synth.sampled_heads(cfg)[0]
@@ -113,17 +112,17 @@ def test_backward_720p_sampled():
     ref = oracle_mask(cfg, qh, kh)
     union = unpack_bits(res["bits"][0, h], nb)
     adapt = unpack_bits(res["abits"][0, h], nb)
-    check_mask_rows(union, adapt, ref, cfg.thr, f"720p bwd h{h}")
+    check_mask_rows(union, adapt, ref, cfg.thr, f"{label} h{h}")
     m = ref["mask"].copy()
     band = (union != m).any(1)
     m[band] = union[band]
     valid = ref["valid"]
     qb, kb, vb, gb = (O.flatten(x, og) for x in (qh, kh, vh, gh))
     rng = np.random.default_rng([cfg.seed, 11])
-    qrows = sorted(set([0, nb - 1] + rng.choice(nb, 4, replace=False).tolist()))
-    kcols = sorted(set([nb - 1, int(rng.integers(nb))]))
+    qrows = sorted(set([0, nb - 1] + rng.choice(nb, n_rows, replace=False).tolist()))
+    kcols = sorted(set([nb - 1] + rng.choice(nb, n_cols, replace=False).tolist()))
     rows = sorted(set(qrows) | set(np.flatnonzero(m[:, kcols].any(1)).tolist()))
-    log(f"720p backward: oracle over {len(rows)} query blocks")
+    log(f"{label}: oracle over {len(rows)} query blocks")
     rdq, rdk, rdv, rlse = O.block_sparse_attention_backward(qb, kb, vb, m, valid, gb, rows=rows)
     dq, dk, dv = (O.flatten(f64(x[0, h]), og) for x in (bw.dq, bw.dk, bw.dv))
     lse_h = lse[0, h].cpu().numpy().astype(np.float64)
@@ -138,7 +137,18 @@ def test_backward_720p_sampled():
                                 (dv, rdv, sel_k, "dv")):
         sc = np.abs(want[sel]).max()
         err = np.abs(got[sel] - want[sel])
-        log(f"720p backward {lab}: max|err| {err.max() / sc:.2e} mean {err.mean() / sc:.2e} "
+        log(f"{label} {lab}: max|err| {err.max() / sc:.2e} mean {err.mean() / sc:.2e} "
             f"(relative to {sc:.3e})")
         assert np.isfinite(got[sel]).all()
         assert err.max() <= 2e-2 * sc and err.mean() <= 2e-3 * sc, lab
+
+
+def test_backward_720p_sampled():
+    """Gradients at the 720p bench shape, all 40 heads."""
+    _backward_sampled(synth.config("720p"), 4, 1, "720p backward")
+
+
+def test_backward_max_blocks_sampled():
+    """Gradients at 3840 blocks per head (64 frames at 720p): the longest
+    transposed mask rows and key-major lists."""
+    _backward_sampled(synth.config("long", T=64, heads=2, thr=0.5), 2, 1, "max_blocks backward")
