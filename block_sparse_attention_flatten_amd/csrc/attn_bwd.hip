@@ -517,7 +517,8 @@ attn_bwd_dkdv_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
         // phase 1: S, then p = exp2(S scale log2(e) - lse log2(e)); the
         // weights of queries 0-31 are computed in the slots of queries 32-63.
         // Pad keys need no mask: a key's weights only reach its own column
-        // of the results, which is never stored.
+        // of the results, which is not stored (natural layout) or stored as
+        // zeros (blocked layout).
         f32x16 sacc[2];
         f32x4 l4[2][4];
 #pragma unroll
