@@ -203,7 +203,7 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
     const bool grow = mx > m_run + 8.0f;
     if (__any(grow)) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);   // 0 on the first block
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first block
       l_run *= alpha;
 #pragma unroll
       for (int t = 0; t < A::kDTiles; ++t) oacc[t] *= alpha;

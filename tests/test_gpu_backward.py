@@ -37,6 +37,7 @@ CASES = {
     "ragged_f32": ("tiny", dict(batch=1, heads=2, T=2, H=11, W=17, head_dim=128, thr=0.7,
                                 sta=(3, 3, 3))),
     "thr_one_bf16": ("small", dict(heads=1, T=2, H=16, W=24, thr=1.0)),
+    "hot_bf16": ("small", dict(heads=2, T=3, H=16, W=24, thr=0.7, sta=(3, 3, 3), gain_qk=8.0)),
 }
 REL = {torch.bfloat16: (2e-2, 2e-3), torch.float32: (1e-4, 1e-5)}
 

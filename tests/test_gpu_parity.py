@@ -28,6 +28,9 @@ CASES = {
     "thr_one": ("small", dict(heads=2, T=2, H=16, W=24, thr=1.0)),
     "thr_low": ("small", dict(heads=2, T=3, H=24, W=24, thr=0.05)),
     "pure_sta": ("small", dict(heads=2, T=3, H=21, W=24, thr=0.0, sta=(3, 3, 3))),
+    # large-magnitude scores (gain 8 on the Q and K fields): deep online-softmax
+    # rescaling, weights spanning many orders of magnitude
+    "hot": ("small", dict(heads=2, T=3, H=16, W=24, thr=0.7, sta=(3, 3, 3), gain_qk=8.0)),
 }
 
 
