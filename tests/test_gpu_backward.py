@@ -38,6 +38,7 @@ CASES = {
                                 sta=(3, 3, 3))),
     "thr_one_bf16": ("small", dict(heads=1, T=2, H=16, W=24, thr=1.0)),
     "hot_bf16": ("small", dict(heads=2, T=3, H=16, W=24, thr=0.7, sta=(3, 3, 3), gain_qk=8.0)),
+    "flat_bf16": ("small", dict(heads=1, T=2, H=16, W=24, thr=0.5, gain_qk=0.0, noise=0.0)),
 }
 REL = {torch.bfloat16: (2e-2, 2e-3), torch.float32: (1e-4, 1e-5)}
 
