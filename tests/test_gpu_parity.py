@@ -34,6 +34,8 @@ CASES = {
     # nearly flat scores (gain 0.02 on the Q and K fields, no noise): the cut
     # falls among near-ties, most rows keep about thr * nb blocks
     "cold": ("small", dict(heads=2, T=3, H=16, W=24, thr=0.6, gain_qk=0.02, noise=0.0)),
+    # asymmetric STA window wider than the grid in some directions
+    "wide_sta": ("small", dict(heads=2, T=5, H=24, W=40, thr=0.3, sta=(5, 1, 7))),
     # Q = K = 0: every score is exactly 0, so every row is a tie of nb blocks
     # broken by block index, and O is the mean of V over the kept keys
     "flat": ("small", dict(heads=2, T=2, H=16, W=24, thr=0.5, gain_qk=0.0, noise=0.0)),
