@@ -178,7 +178,9 @@ int nabla_compact(const nabla_geom* geom, const uint32_t* mask_bits,
  * in geom's layout and out_dtype;
  * in NABLA_LAYOUT_BLOCKED pad query slots of o are written as zeros.  A row
  * with an empty list produces zeros.  scale > 0 (usually 1/sqrt(d)).
- * col_idx entries must lie in [0, nb). */
+ * col_idx entries must lie in [0, nb); the kernels do not fault on bad lists:
+ * an entry outside [0, nb) is skipped, and a row whose pointers are negative,
+ * decreasing or past nb * nb is treated as empty. */
 int nabla_attn_fwd(const nabla_geom* geom, const void* q, const void* k,
                    const void* v, const int32_t* row_ptr, const int32_t* col_idx,
                    float scale, void* o, void* stream);

@@ -293,3 +293,59 @@ def test_transpose_v_and_attn_fwd_vt(case):
         torch.cuda.synchronize()
         iv = torch.int32 if odt == torch.float32 else torch.int16
         assert torch.equal(o_vt.view(iv), o_tr.view(iv)), f"{name}: V^T path differs ({odt})"
+
+
+@pytest.mark.parametrize("path", ["vt", "tr", "f32"])
+def test_out_of_range_list_entries_are_skipped(path):
+    """The attention kernels skip list entries outside [0, nb) and treat a row
+    whose end pointer lies past the list capacity as empty: corrupted lists
+    give exactly the output of the same lists with those entries removed
+    (and that row emptied)."""
+    f32 = path == "f32"
+    cfg = synth.config("tiny" if f32 else "small", heads=2, T=3, H=16, W=24, thr=0.6,
+                       sta=(3, 3, 3), head_dim=64 if f32 else 128)
+    q, k, v = synth.make_qkv(cfg, device="cuda")
+    res = run_pipeline(cfg, q, k, v, out_dtype=q.dtype, attn="tr" if path == "tr" else "vt")
+    g = res["g"]
+    nb = g.nb
+    rp, ci = res["rp"].cpu().numpy(), res["ci"].cpu().numpy()
+    bad_rp, bad_ci = rp.copy(), ci.copy()
+    clean_rp, clean_ci = np.zeros_like(rp), np.full_like(ci, -7)
+    for i in range(rp.shape[0]):
+        rows = []
+        for r in range(nb):
+            lst = ci[i, rp[i, r]:rp[i, r + 1]].tolist()
+            keep = list(lst)
+            if r in (1, 5, 7) and len(lst) >= 2:          # overwrite the second entry
+                bad_ci[i, rp[i, r] + 1] = {1: -1, 5: nb, 7: 1 << 30}[r]
+                keep = lst[:1] + lst[2:]
+            if r == nb - 1:                                # end pointer past the capacity
+                bad_rp[i, nb] = nb * nb + 5
+                keep = []
+            rows.append(keep)
+        pos = 0
+        for r, keep in enumerate(rows):
+            clean_rp[i, r] = pos
+            clean_ci[i, pos:pos + len(keep)] = keep
+            pos += len(keep)
+        clean_rp[i, nb] = pos
+    d = cfg.head_dim
+    scale = 1.0 / math.sqrt(d)
+    outs = []
+    for p_, c_ in ((bad_rp, bad_ci), (clean_rp, clean_ci)):
+        rpt, cit = torch.from_numpy(p_).cuda(), torch.from_numpy(c_).cuda()
+        o = torch.full_like(q, 3.0)
+        if path == "vt":
+            vt = torch.empty(nabla.vt_shape(g), dtype=q.dtype, device="cuda")
+            nabla.nabla_transpose_v(g, v, vt)
+            nabla.nabla_attn_fwd_vt(g, q, k, vt, rpt, cit, scale, o)
+        else:
+            nabla.nabla_attn_fwd(g, q, k, v, rpt, cit, scale, o)
+        torch.cuda.synchronize()
+        outs.append(o)
+    iv = torch.int16 if q.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(outs[0].view(iv), outs[1].view(iv)), f"{path}: corrupted lists differ"
+    # the emptied last row gives zeros at its valid queries
+    og = ogeom(cfg)
+    last = O.flatten(f64(outs[1][0, 0]), og)[nb - 1][O.valid_tokens(og)[nb - 1]]
+    assert np.all(last == 0)
