@@ -59,6 +59,8 @@ def parse():
                     help="skip the dense reference (the same kernel with every block kept)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--serial", action="store_true",
+                    help="run every stage of the step on one stream (no V^T overlap)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the achievable matrix-core / copy rate measurements")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -318,13 +320,27 @@ def main():
         else:
             nabla.nabla_attn_fwd(g, q, k, v, rp, ci, scale, o, stream)
 
+    # V^T is written on a second stream (default priority) beside the mask
+    # kernel: the HBM-bound copy overlaps the compute-bound reduced map.  It
+    # starts after the step's pooling, i.e. after the previous step's
+    # attention has finished reading V^T.
+    side = torch.cuda.Stream() if vt_path and not args.serial else None
+    pooled, vt_done = torch.cuda.Event(), torch.cuda.Event()
+
     def step(marks=None):
         if marks is not None:
             marks[0].record(stream)
         nabla.nabla_pool(g, q, k, qbar, kbar, stream)
+        if side is not None:
+            pooled.record(stream)
+            side.wait_event(pooled)
+            nabla.nabla_transpose_v(g, v, vt, side)
+            vt_done.record(side)
         nabla.nabla_mask(g, qbar, kbar, thr, sta, bits, cnt, None, stream)
         nabla.nabla_compact(g, bits, cnt, rp, ci, stream)
-        if vt_path:
+        if side is not None:
+            stream.wait_event(vt_done)
+        elif vt_path:
             nabla.nabla_transpose_v(g, v, vt, stream)
         if marks is not None:
             marks[1].record(stream)
