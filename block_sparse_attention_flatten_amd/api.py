@@ -392,3 +392,60 @@ def backward(g: Geometry, q, k, v, o, lse, dout, mask_bits, row_ptr, col_idx,
     nabla_attn_bwd_dq(g, q, k, v, o, dout, lse, row_ptr, col_idx, scale, dq, delta, stream)
     nabla_attn_bwd_dkdv(g, q, k, v, dout, lse, delta, col_ptr, row_idx, scale, dk, dv, stream)
     return BackwardResult(dq, dk, dv, delta, col_ptr, row_idx)
+
+
+# ---------------------------------------------------------------------------
+# autograd: the attention call as a differentiable torch op (mask held fixed)
+# ---------------------------------------------------------------------------
+class NablaAttention(torch.autograd.Function):
+    """o = NABLA attention of THW tensors q, k, v [B, heads, T, H, W, d]
+    (bf16 or float32, contiguous).  Forward: nabla_pool, nabla_mask,
+    nabla_compact and the attention with its log-sum-exp; backward: the
+    gradient calls of ``backward`` with the forward's mask held fixed (the
+    mask is a threshold, so thr and sta get no gradient)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, thr, sta, scale):
+        B, h, T, H, W, d = q.shape
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        g = Geometry(B, h, T, H, W, d, q.dtype)
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        dev = q.device
+        nb = g.nb
+        qbar = torch.empty((B, h, nb, d), dtype=torch.float32, device=dev)
+        kbar = torch.empty_like(qbar)
+        bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)
+        rp = torch.empty((B * h, nb + 1), dtype=torch.int32, device=dev)
+        ci = torch.empty((B * h, nb * nb), dtype=torch.int32, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(lse_shape(g), dtype=torch.float32, device=dev)
+        nabla_pool(g, q, k, qbar, kbar)
+        nabla_mask(g, qbar, kbar, thr, sta, bits, cnt, None)
+        nabla_compact(g, bits, cnt, rp, ci)
+        if q.dtype == torch.bfloat16:
+            vt = torch.empty(vt_shape(g), dtype=q.dtype, device=dev)
+            nabla_transpose_v(g, v, vt)
+            nabla_attn_fwd_vt_lse(g, q, k, vt, rp, ci, scale, o, lse)
+        else:
+            nabla_attn_fwd_lse(g, q, k, v, rp, ci, scale, o, lse)
+        ctx.save_for_backward(q, k, v, o, lse, bits, rp, ci)
+        ctx.geom, ctx.scale = g, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, o, lse, bits, rp, ci = ctx.saved_tensors
+        res = backward(ctx.geom, q, k, v, o, lse, dout.contiguous().to(q.dtype), bits, rp, ci,
+                       ctx.scale)
+        return res.dq, res.dk, res.dv, None, None, None
+
+
+def nabla_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, thr: float,
+                    sta: Optional[Sequence[int]] = (3, 3, 3),
+                    scale: Optional[float] = None) -> torch.Tensor:
+    """Differentiable NABLA attention on THW tensors (see NablaAttention)."""
+    return NablaAttention.apply(q, k, v, thr, sta, scale)
+
+
+__all__ += ["NablaAttention", "nabla_attention"]

@@ -166,3 +166,23 @@ def test_backward_rejects_mixed_dtypes():
     with pytest.raises(nabla.NablaError) as e:   # the C ABI's dtype check, before any launch
         nabla.nabla_attn_bwd_dq(g, x, x, x, x, x, lse, rp, ci, 0.125, x, lse)
     assert e.value.status == -3
+
+
+@pytest.mark.parametrize("name", ["ragged_bf16", "ragged_f32"])
+def test_autograd_function_matches_explicit_calls(name):
+    """nabla_attention as a torch autograd op: its output and the gradients
+    autograd returns equal, bit for bit, the explicit forward-with-lse and
+    backward calls on the same inputs."""
+    base, kw = CASES[name]
+    cfg = synth.config(base, **kw)
+    q0, k0, v0 = synth.make_qkv(cfg, device="cuda")
+    dout = synth.make_tensor(cfg, 3, device="cuda")
+    q, k, v = (x.clone().requires_grad_(True) for x in (q0, k0, v0))
+    o = nabla.nabla_attention(q, k, v, cfg.thr, cfg.sta)
+    (o.float() * dout.float()).sum().backward()
+    torch.cuda.synchronize()
+    g, _, _, _, _, o_ref, _, _, bw, _, _ = _run(cfg, nabla.LAYOUT_THW)
+    iv = torch.int16 if q0.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(o.detach().view(iv), o_ref.view(iv))
+    for got, ref, lab in ((q.grad, bw.dq, "dq"), (k.grad, bw.dk, "dk"), (v.grad, bw.dv, "dv")):
+        assert torch.equal(got.view(iv), ref.view(iv)), f"{name}: autograd {lab} differs"
