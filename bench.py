@@ -159,6 +159,12 @@ def torch_flash_reference(torch, cfg, q, k, v, time_call, attn_ms):
         with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
             ms = time_call(lambda: torch.nn.functional.scaled_dot_product_attention(qs, ks, vs),
                            reps=3)
+            # its backward on a synthetic dO (graph kept, gradients accumulate)
+            qg, kg, vg = (x.detach().clone().requires_grad_(True) for x in (qs, ks, vs))
+            og = torch.nn.functional.scaled_dot_product_attention(qg, kg, vg)
+            dout = torch.ones_like(og)
+            bwd_ms = time_call(lambda: og.backward(dout, retain_graph=True), reps=2)
+            del qg, kg, vg, og, dout
     except RuntimeError as e:
         log(f"torch flash reference unavailable: {e}")
         return None
@@ -166,7 +172,9 @@ def torch_flash_reference(torch, cfg, q, k, v, time_call, attn_ms):
     out = {"what": "torch scaled_dot_product_attention, flash backend, full attention over "
                    "the valid tokens", "ms": round(ms, 3),
            "tflops_valid_tokens": round(flops / (ms * 1e-3) / 1e12, 1),
-           "speedup_sparse_vs_torch_flash": round(ms / attn_ms, 3)}
+           "speedup_sparse_vs_torch_flash": round(ms / attn_ms, 3),
+           "backward_ms": round(bwd_ms, 3),
+           "backward_tflops_valid_tokens": round(2.5 * flops / (bwd_ms * 1e-3) / 1e12, 1)}
     log(f"torch flash reference: {out}")
     return out
 
@@ -543,8 +551,11 @@ def main():
         }
         log(f"dense reference: {dense_ms:.2f} ms ({result['dense_reference']['tflops']} TFLOP/s)")
         del rp_full, ci_full
-        result["dense_reference"]["torch_sdpa_flash"] = torch_flash_reference(
-            torch, cfg, q, k, v, time_call, attn_avg)
+        tf = torch_flash_reference(torch, cfg, q, k, v, time_call, attn_avg)
+        if tf is not None and "backward" in result:
+            tf["speedup_sparse_backward_vs_torch_flash"] = round(
+                tf["backward_ms"] / result["backward"]["ms"], 3)
+        result["dense_reference"]["torch_sdpa_flash"] = tf
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, thr, sta, args.cpu_seconds)
