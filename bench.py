@@ -21,6 +21,8 @@ import platform
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -59,6 +61,9 @@ def parse():
                     help="skip the dense reference (the same kernel with every block kept)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--layer", action="store_true",
+                    help="also time a Wan-shaped attention layer (QKV and output projections "
+                         "on hipBLASLt around the NABLA call, tokens in the blocked order)")
     ap.add_argument("--serial", action="store_true",
                     help="run every stage of the step on one stream (no V^T overlap)")
     ap.add_argument("--no-peaks", action="store_true",
@@ -177,6 +182,118 @@ def torch_flash_reference(torch, cfg, q, k, v, time_call, attn_ms):
            "backward_tflops_valid_tokens": round(2.5 * flops / (bwd_ms * 1e-3) / 1e12, 1)}
     log(f"torch flash reference: {out}")
     return out
+
+
+def layer_leg(torch, nabla, cfg, g, x_field, thr, sta, scale, time_call, dev):
+    """One self-attention layer of a Wan-shaped DiT around the NABLA call,
+    with the token sequence kept in the blocked (fractal-flattened) order
+    across the network, so no reorder runs per layer: X [S, h d] ->
+    QKV = X W_qkv (one hipBLASLt GEMM through torch.matmul) -> head-major
+    copies -> NABLA (pool, mask, compact, V^T, attention; blocked layout) ->
+    token-major copy -> O W_o.  Random weights; X is the bench's synthetic Q
+    field, reordered once; pad tokens of the blocked order are zero.  Same layer with torch's flash SDPA in place
+    of NABLA for comparison (tokens of the valid set only)."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    if cfg.torch_dtype != torch.bfloat16 or cfg.batch != 1:
+        return None
+    h, d, nb = cfg.heads, cfg.head_dim, g.nb
+    S = nb * 64                                   # blocked order, pad slots included
+    D = h * d
+    # X: the smooth spatio-temporal synthetic field of the bench's Q (40 x 128
+    # channels) in the blocked token order, so that the projected Q and K keep
+    # a latent-local structure; random N(0, 1/D) weights
+    xb = torch.zeros(g.tensor_shape(nabla.LAYOUT_BLOCKED), dtype=torch.bfloat16, device=dev)
+    nabla.nabla_flatten(g, x_field, xb)
+    X = xb.view(h, S, d).permute(1, 0, 2).reshape(S, D).contiguous()
+    del xb
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    Wqkv = (torch.randn(D, 3 * D, generator=gen, device=dev) / math.sqrt(D)).to(torch.bfloat16)
+    Wo = (torch.randn(D, D, generator=gen, device=dev) / math.sqrt(D)).to(torch.bfloat16)
+    gb = g.with_layout(nabla.LAYOUT_BLOCKED)
+    qbar = torch.empty((1, h, nb, d), dtype=torch.float32, device=dev)
+    kbar = torch.empty_like(qbar)
+    bits = torch.empty((1, h, nb, g.nw), dtype=torch.int32, device=dev)
+    cnt = torch.empty((1, h, nb), dtype=torch.int32, device=dev)
+    rp = torch.empty((h, nb + 1), dtype=torch.int32, device=dev)
+    ci = torch.empty((h, nb * nb), dtype=torch.int32, device=dev)
+    vt = torch.empty(nabla.vt_shape(gb), dtype=torch.bfloat16, device=dev)
+    st = {}
+
+    def proj_in():
+        qkv = X @ Wqkv                            # [S, 3 h d]
+        st["qkv"] = qkv.view(S, 3, h, d).permute(1, 2, 0, 3).contiguous()   # [3, h, S, d]
+
+    def attention():
+        q, k, v = (st["qkv"][i].view(1, h, nb, 64, d) for i in range(3))
+        o = torch.empty_like(q)
+        nabla.nabla_pool(gb, q, k, qbar, kbar)
+        nabla.nabla_mask(gb, qbar, kbar, thr, sta, bits, cnt, None)
+        nabla.nabla_compact(gb, bits, cnt, rp, ci)
+        nabla.nabla_transpose_v(gb, v, vt)
+        nabla.nabla_attn_fwd_vt(gb, q, k, vt, rp, ci, scale, o)
+        st["o"] = o
+
+    def proj_out():
+        st["y"] = st["o"].view(h, S, d).permute(1, 0, 2).reshape(S, D) @ Wo
+
+    def layer():
+        proj_in()
+        attention()
+        proj_out()
+
+    layer()
+    ms = {"qkv_projection_and_head_major_copy": time_call(proj_in, reps=3),
+          "nabla_attention": time_call(attention, reps=3),
+          "token_major_copy_and_output_projection": time_call(proj_out, reps=3),
+          "layer": time_call(layer, reps=3)}
+    # the same layer with dense flash attention over the valid tokens
+    valid = torch.from_numpy(np.ascontiguousarray(valid_slots(cfg, nb))).to(dev)
+    sv = int(valid.sum())
+
+    def dense_attention():
+        q, k, v = (st["qkv"][i][:, valid].unsqueeze(0) for i in range(3))   # [1, h, Sv, d]
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            od = torch.nn.functional.scaled_dot_product_attention(q, k, v)
+        o = torch.zeros((h, S, d), dtype=torch.bfloat16, device=dev)
+        o[:, valid] = od[0]
+        st["o"] = o
+
+    def dense_layer():
+        proj_in()
+        dense_attention()
+        proj_out()
+
+    try:
+        dense_ms = time_call(dense_layer, reps=2)
+    except RuntimeError as e:
+        log(f"dense layer reference unavailable: {e}")
+        dense_ms = None
+    layer()                                       # the call's own mask, for its sparsity
+    torch.cuda.synchronize()
+    sparsity = 1.0 - int(cnt.to(torch.int64).sum()) / (h * nb * nb)
+    out = {"what": "Wan-shaped self-attention layer, tokens in the blocked order (flattened "
+                   "once per network): QKV projection, NABLA, output projection",
+           "tokens_blocked": S, "model_dim": D, "sparsity": round(sparsity, 4),
+           "ms": {k_: round(v_, 3) for k_, v_ in ms.items()},
+           "attention_share": round(ms["nabla_attention"] / ms["layer"], 3),
+           "dense_flash_layer_ms": None if dense_ms is None else round(dense_ms, 3),
+           "layer_speedup_vs_dense_flash": None if dense_ms is None
+           else round(dense_ms / ms["layer"], 3)}
+    log(f"dit layer: {out}")
+    del X, Wqkv, Wo, st
+    return out
+
+
+def valid_slots(cfg, nb):
+    """Valid-token flags of the blocked order, [nb * 64] (pad slots False)."""
+    gh, gw = -(-cfg.H // 8), -(-cfg.W // 8)
+    b = np.arange(nb)
+    hb, wb = (b // gw) % gh, b % gw
+    s = np.arange(64)
+    rows = hb[:, None] * 8 + s[None, :] // 8
+    cols = wb[:, None] * 8 + s[None, :] % 8
+    return ((rows < cfg.H) & (cols < cfg.W)).reshape(-1)
 
 
 KERNEL_SOURCES = ("attn_fwd_vt.hip", "attn_common.hpp", "nabla_common.hpp")
@@ -556,6 +673,8 @@ def main():
             tf["speedup_sparse_backward_vs_torch_flash"] = round(
                 tf["backward_ms"] / result["backward"]["ms"], 3)
         result["dense_reference"]["torch_sdpa_flash"] = tf
+    if args.layer:
+        result["dit_layer"] = layer_leg(torch, nabla, cfg, g, q, thr, sta, scale, time_call, dev)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, thr, sta, args.cpu_seconds)
