@@ -350,10 +350,13 @@ def algorithmic_bytes(cfg, nb, nnz_total):
     return pool, mask, compact
 
 
-def cpu_baseline(cfg, q, k, v, thr, sta, budget_s):
+def cpu_baseline(cfg, q, k, v, thr, sta, budget_s, gpu_bits=None, gpu_o=None):
     """Time the float64 oracle on a bounded sample of the same workload: one
     head's full mask construction plus attention for as many query blocks as
-    fit in the time budget, extrapolated to the whole call."""
+    fit in the time budget, extrapolated to the whole call.  Given the GPU's
+    mask words and output of head 0, also report (after the timing) how they
+    compare with the oracle's: band rows, differing rows, output error on the
+    sampled query blocks."""
     import numpy as np
     import oracle as O
     try:
@@ -369,26 +372,49 @@ def cpu_baseline(cfg, q, k, v, thr, sta, budget_s):
     t0 = time.perf_counter()
     valid = O.valid_tokens(g)
     qb, kb, vb = O.flatten(qh, g), O.flatten(kh, g), O.flatten(vh, g)
-    m, _, _ = O.nabla_mask(O.pool(qb, valid), O.pool(kb, valid), thr, g, sta)
+    m, m_ad, p = O.nabla_mask(O.pool(qb, valid), O.pool(kb, valid), thr, g, sta)
     t_mask = time.perf_counter() - t0
     rng = np.random.default_rng(0)
     order = rng.permutation(g.nb)
     done, t_attn, kept_pairs = 0, 0.0, 0
+    outs = []
     while done < g.nb and t_mask + t_attn < budget_s:
         rows = order[done:done + 16]
         t1 = time.perf_counter()
-        O.block_sparse_attention(qb, kb, vb, m, valid, rows=rows)
+        ob = O.block_sparse_attention(qb, kb, vb, m, valid, rows=rows)
         t_attn += time.perf_counter() - t1
+        outs.append((rows, ob))
         kept_pairs += int(m[rows].sum())
         done += len(rows)
     per_head = t_mask + t_attn * g.nb / done
     seconds = per_head * cfg.heads * cfg.batch
     flops_head = int(m.sum()) * 4 * 64 * 64 * cfg.head_dim
+    accuracy = None
+    if gpu_bits is not None and gpu_o is not None:
+        words = gpu_bits.astype(np.uint32)
+        gm = ((words[:, np.arange(g.nb) >> 5] >> (np.arange(g.nb) & 31)) & 1).astype(bool)
+        band_a, band_b = O.band_rows(p, m_ad, thr)
+        band = band_a | band_b
+        diff = (gm != m).any(1)
+        got = O.flatten(gpu_o, g)
+        errs = []
+        for rows, ob in outs:
+            for r in rows:
+                if not diff[r]:                       # rows whose masks agree
+                    errs.append(np.abs(got[r][valid[r]] - ob[r][valid[r]]))
+        e = np.concatenate([x.ravel() for x in errs]) if errs else np.zeros(1)
+        accuracy = {"head": h, "band_rows_a": int(band_a.sum()), "band_rows_b": int(band_b.sum()),
+                    "differing_rows": int(diff.sum()),
+                    "differing_rows_outside_band": int((diff & ~band).sum()),
+                    "output_rows_compared": int(sum(1 for rows, _ in outs for r in rows
+                                                    if not diff[r])),
+                    "max_abs_err": float(e.max()), "mean_abs_err": float(e.mean())}
     return {
         "value": flops_head * cfg.heads * cfg.batch / seconds / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
+        "accuracy_vs_gpu": accuracy,
         "sample": (f"float64 oracle, head 0 of {cfg.heads}: full mask construction "
                    f"({g.nb} rows) + attention for {done} of {g.nb} query blocks "
                    f"({t_mask + t_attn:.1f} s CPU); extrapolated to the whole call "
@@ -676,9 +702,14 @@ def main():
     if args.layer:
         result["dit_layer"] = layer_leg(torch, nabla, cfg, g, q, thr, sta, scale, time_call, dev)
     if not args.no_cpu_baseline:
+        step()                       # the call's own mask and output again (the legs above
+        torch.cuda.synchronize()     # reused the buffers)
         log("cpu baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, thr, sta, args.cpu_seconds)
-        log(f"cpu baseline done: {result['cpu_baseline']['value']:.6f} TFLOP/s")
+        result["cpu_baseline"] = cpu_baseline(
+            cfg, q, k, v, thr, sta, args.cpu_seconds,
+            gpu_bits=bits[0, 0].cpu().numpy(), gpu_o=o[0, 0].double().cpu().numpy())
+        log(f"cpu baseline done: {result['cpu_baseline']['value']:.6f} TFLOP/s; "
+            f"head 0 vs the oracle: {result['cpu_baseline']['accuracy_vs_gpu']}")
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
