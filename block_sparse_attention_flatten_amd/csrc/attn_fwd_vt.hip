@@ -336,14 +336,16 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
   // exponentials of elements r, r + 1 of sc[kt] into the bf16 operand P^T;
   // the row sum adds the rounded values (bf16 pairs summed by v_dot2_f32_bf16)
   // (m_ref = +inf gives exact zeros: scores are always finite here).  The
-  // empty asm statement pins the work to its slot of the schedule.
+  // slot's scheduling barrier keeps this work in its slot; inside the slot
+  // the compiler puts the operand read between the exponentials and their
+  // first use, which the transcendental-result hazard would otherwise fill
+  // with a wait state.
   auto exp_pair = [&](const f32x16 (&sc)[2], bf16x8 (&pop)[2][2], int kt, int r, float m_ref) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     const float x0 = __builtin_fmaf(sc[kt][r], scale_log2, -m_ref);
     const float x1 = __builtin_fmaf(sc[kt][r + 1], scale_log2, -m_ref);
     const bf16x2 pr = {(__bf16)__builtin_amdgcn_exp2f(x0), (__bf16)__builtin_amdgcn_exp2f(x1)};
     l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
-    asm volatile("" ::"v"(pr));
     pop[kt][r >> 3][r & 7] = pr[0];
     pop[kt][r >> 3][(r & 7) + 1] = pr[1];
   };
