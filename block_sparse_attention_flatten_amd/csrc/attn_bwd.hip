@@ -174,16 +174,26 @@ __device__ inline bf16x8 sw_row_read(int tb, int row, int st, int hl) {
 // 4e + i / 4, so the lane supplying rows k0 + s / 4 and k0 + 8 + s / 4
 // (k0 = row0 + 16 h + 4 hl), columns 32 dt + (lane & 16) + 4 (s % 4), yields
 // exactly the k order of a B operand built from a 32 x 32 accumulator.
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16) at base + off.  Through
+// the restrict parameter the inlined read carries an alias scope, and the
+// compiler's wait insertion then stops treating it as a possible reader of
+// every direct-to-LDS load still in flight: without it, each step's first
+// transposing read waited (vmcnt(0)) for the NEXT step's tile loads, so they
+// had only the first half of a step to land.  The kernels order their reads
+// after the loads they read by their own waits and barriers.
+__device__ inline bf16x4 lds_read_tr8(lds_char* __restrict__ base, int off) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + off));
+}
+
 template <int D>
 __device__ inline bf16x8 sw_tr_read(int tb, int row0, int h, int dt, int lane) {
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
   const int col = 32 * dt + (lane & 16) + 4 * (lane & 3);
   const int r = row0 + 16 * h + 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int c = (col & 7) * 2;
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4*)(uintptr_t)(tb + SwTile<D>::addr(r, col >> 3) + c));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4*)(uintptr_t)(tb + SwTile<D>::addr(r + 8, col >> 3) + c));
+  lds_char* const base = (lds_char*)(uintptr_t)tb;
+  const bf16x4 lo = lds_read_tr8(base, SwTile<D>::addr(r, col >> 3) + c);
+  const bf16x4 hi = lds_read_tr8(base, SwTile<D>::addr(r + 8, col >> 3) + c);
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
