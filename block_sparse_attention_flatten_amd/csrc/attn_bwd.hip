@@ -105,9 +105,15 @@ __device__ inline void store_row(__bf16* dst, const f32x16 (&acc)[D / 32], float
 // ---- swizzled tiles filled by direct-to-LDS loads ----
 // A 64 x D bf16 tile whose 16-byte chunks are permuted within each row so that
 // the 16-byte row reads of 16 consecutive rows (one logical chunk) hit
-// distinct banks: 256-byte rows (D = 128) use chunk ^ (r & 7) plus 128 bytes
-// of padding after every 8 rows; 128-byte rows (D = 64) use chunk ^
-// ((r & 7) ^ ((r >> 3) & 1)).  The tile is filled in 1-KB direct loads:
+// distinct banks: 256-byte rows (D = 128) use chunk ^ g(r) plus 128 bytes of
+// padding after every 8 rows; 128-byte rows (D = 64) use chunk ^
+// ((r & 7) ^ ((r >> 3) & 1)).  g(r) = ((r & 3) << 1) | ((r >> 2) & 1) permutes
+// each 8-row group (row reads stay conflict-free) and also gives 4
+// consecutive rows distinct values of g >> 1, so the transposing reads, where
+// 16 lanes take chunks 2m and 2m + 1 of 4 consecutive rows, hit 8 distinct
+// bank groups; with r & 7 rows 2k and 2k + 1 collided, and the bank-conflict
+// counter read about half of the LDS-active cycles in both kernels.  The
+// tile is filled in 1-KB direct loads:
 // lane l of a load writes bytes 16 l .. 16 l + 15 of it and reads the global
 // chunk that belongs there.
 template <int D>
@@ -116,7 +122,9 @@ struct SwTile {
   static constexpr int kGroupBytes = kWide ? 8 * 256 + 128 : 8 * 128;   // 8 rows
   static constexpr int kBytes = 8 * kGroupBytes;
   static constexpr int kOps = kN * D * 2 / 1024;          // 1-KB loads per tile
-  __device__ static int swz(int r) { return kWide ? (r & 7) : ((r & 7) ^ ((r >> 3) & 1)); }
+  __device__ static int swz(int r) {
+    return kWide ? (((r & 3) << 1) | ((r >> 2) & 1)) : ((r & 7) ^ ((r >> 3) & 1));
+  }
   // byte offset of logical chunk c of row r
   __device__ static int addr(int r, int c) {
     return (r >> 3) * kGroupBytes + (r & 7) * (2 * D) + ((c ^ swz(r)) << 4);
