@@ -175,13 +175,6 @@ __device__ inline bf16x8 sw_row_read(int tb, int row, int st, int hl) {
   return lds_read16(tb + SwTile<D>::addr(row, 2 * st + hl));
 }
 
-// A operand of acc[dt] += X^T[32 dt + lane % 32][rows] * B over the 16 tile
-// rows row0 + 16 h .. + 15 of the swizzled tile at LDS address tb (the
-// product over tile rows, X^T from transpose loads).  In each 16-lane group,
-// lane i receives element i % 4 of the 4-element rows addressed by lanes
-// 4e + i / 4, so the lane supplying rows k0 + s / 4 and k0 + 8 + s / 4
-// (k0 = row0 + 16 h + 4 hl), columns 32 dt + (lane & 16) + 4 (s % 4), yields
-// exactly the k order of a B operand built from a 32 x 32 accumulator.
 // Transposing 8-byte LDS read (ds_read_b64_tr_b16) at base + off.  Through
 // the restrict parameter the inlined read carries an alias scope, and the
 // compiler's wait insertion then stops treating it as a possible reader of
@@ -194,6 +187,13 @@ __device__ inline bf16x4 lds_read_tr8(lds_char* __restrict__ base, int off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + off));
 }
 
+// A operand of acc[dt] += X^T[32 dt + lane % 32][rows] * B over the 16 tile
+// rows row0 + 16 h .. + 15 of the swizzled tile at LDS address tb (the
+// product over tile rows, X^T from transpose loads).  In each 16-lane group,
+// lane i receives element i % 4 of the 4-element rows addressed by lanes
+// 4e + i / 4, so the lane supplying rows k0 + s / 4 and k0 + 8 + s / 4
+// (k0 = row0 + 16 h + 4 hl), columns 32 dt + (lane & 16) + 4 (s % 4), yields
+// exactly the k order of a B operand built from a 32 x 32 accumulator.
 template <int D>
 __device__ inline bf16x8 sw_tr_read(int tb, int row0, int h, int dt, int lane) {
   const int col = 32 * dt + (lane & 16) + 4 * (lane & 3);
