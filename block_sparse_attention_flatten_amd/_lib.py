@@ -46,6 +46,8 @@ SIGNATURES = {
     "nabla_pool": ([_G, _P, _P, _P, _P, _P], ctypes.c_int),
     "nabla_mask": ([_G, _P, _P, ctypes.c_float, _I32P, _P, _P, _P, _P], ctypes.c_int),
     "nabla_compact": ([_G, _P, _P, _P, _P, _P], ctypes.c_int),
+    "nabla_mask_build": ([_G, _P, _P, ctypes.c_float, _I32P, _P, _P, _P, _P, _P, _P, _P, _P],
+                         ctypes.c_int),
     "nabla_attn_fwd": ([_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
     "nabla_transpose_v": ([_G, _P, _P, _P], ctypes.c_int),
     "nabla_attn_fwd_vt": ([_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),

@@ -23,7 +23,8 @@ from ._lib import DTYPE_BF16, DTYPE_F32, LAYOUT_BLOCKED, LAYOUT_THW, nabla_geom
 
 __all__ = [
     "NablaError", "Geometry", "nabla_num_blocks", "nabla_flatten", "nabla_unflatten",
-    "nabla_pool", "nabla_mask", "nabla_compact", "nabla_attn_fwd", "nabla_transpose_v",
+    "nabla_pool", "nabla_mask", "nabla_compact", "nabla_mask_build", "nabla_attn_fwd",
+    "nabla_transpose_v",
     "nabla_attn_fwd_vt", "nabla_forward_workspace_size", "nabla_forward", "nabla_status_string",
     "nabla_attn_fwd_lse", "nabla_attn_fwd_vt_lse", "nabla_mask_transpose", "nabla_attn_bwd_dq",
     "nabla_attn_bwd_dkdv", "forward", "backward", "vt_shape", "lse_shape",
@@ -190,6 +191,24 @@ def nabla_compact(g: Geometry, mask_bits, row_count, row_ptr, col_idx, stream=No
         _ptr(row_ptr, "row_ptr", (bh, g.nb + 1), torch.int32),
         _ptr(col_idx, "col_idx", (bh, g.nb * g.nb), torch.int32), _stream(stream)),
         "nabla_compact")
+
+
+def nabla_mask_build(g: Geometry, q, k, thr: float, sta, qbar, kbar, mask_bits, row_count,
+                     adaptive_bits, row_ptr, col_idx, stream=None) -> None:
+    shp = g.tensor_shape()
+    pshape = (g.batch, g.heads, g.nb, g.head_dim)
+    mshape = (g.batch, g.heads, g.nb, g.nw)
+    bh = g.batch * g.heads
+    _check(_lib.load().nabla_mask_build(
+        ctypes.byref(g.c()), _ptr(q, "q", shp, g.dtype), _ptr(k, "k", shp, g.dtype), float(thr),
+        _sta(sta), _ptr(qbar, "qbar", pshape, torch.float32),
+        _ptr(kbar, "kbar", pshape, torch.float32),
+        _ptr(mask_bits, "mask_bits", mshape, torch.int32),
+        _ptr(row_count, "row_count", (g.batch, g.heads, g.nb), torch.int32),
+        _ptr(adaptive_bits, "adaptive_bits", mshape, torch.int32),
+        _ptr(row_ptr, "row_ptr", (bh, g.nb + 1), torch.int32),
+        _ptr(col_idx, "col_idx", (bh, g.nb * g.nb), torch.int32), _stream(stream)),
+        "nabla_mask_build")
 
 
 def nabla_attn_fwd(g: Geometry, q, k, v, row_ptr, col_idx, scale: float, o, stream=None) -> None:
@@ -399,8 +418,8 @@ def backward(g: Geometry, q, k, v, o, lse, dout, mask_bits, row_ptr, col_idx,
 # ---------------------------------------------------------------------------
 class NablaAttention(torch.autograd.Function):
     """o = NABLA attention of THW tensors q, k, v [B, heads, T, H, W, d]
-    (bf16 or float32, contiguous).  Forward: nabla_pool, nabla_mask,
-    nabla_compact and the attention with its log-sum-exp; backward: the
+    (bf16 or float32, contiguous).  Forward: nabla_mask_build (pooling, mask,
+    lists) and the attention with its log-sum-exp; backward: the
     gradient calls of ``backward`` with the forward's mask held fixed (the
     mask is a threshold, so thr and sta get no gradient)."""
 
@@ -420,9 +439,7 @@ class NablaAttention(torch.autograd.Function):
         ci = torch.empty((B * h, nb * nb), dtype=torch.int32, device=dev)
         o = torch.empty_like(q)
         lse = torch.empty(lse_shape(g), dtype=torch.float32, device=dev)
-        nabla_pool(g, q, k, qbar, kbar)
-        nabla_mask(g, qbar, kbar, thr, sta, bits, cnt, None)
-        nabla_compact(g, bits, cnt, rp, ci)
+        nabla_mask_build(g, q, k, thr, sta, qbar, kbar, bits, cnt, None, rp, ci)
         if q.dtype == torch.bfloat16:
             vt = torch.empty(vt_shape(g), dtype=q.dtype, device=dev)
             nabla_transpose_v(g, v, vt)

@@ -238,6 +238,27 @@ int nabla_compact(const nabla_geom* geom, const uint32_t* mask_bits, const int32
       nabla::launch_compact(g, mask_bits, row_count, row_ptr, col_idx, as_stream(stream)));
 }
 
+int nabla_mask_build(const nabla_geom* geom, const void* q, const void* k, float thr,
+                     const int32_t* sta, float* qbar, float* kbar, uint32_t* mask_bits,
+                     int32_t* row_count, uint32_t* adaptive_bits, int32_t* row_ptr,
+                     int32_t* col_idx, void* stream) {
+  Geo g;
+  bool empty;
+  int st = make_geo(geom, true, &g, &empty);
+  if (st != NABLA_OK) return st;
+  int win[3];
+  st = check_sta(sta, win);
+  if (st != NABLA_OK) return st;
+  if (!thr_ok(thr, win)) return NABLA_E_THR;
+  if (empty) return NABLA_OK;
+  if (q == nullptr || k == nullptr || qbar == nullptr || kbar == nullptr ||
+      mask_bits == nullptr || row_count == nullptr || row_ptr == nullptr || col_idx == nullptr)
+    return NABLA_E_NULL;
+  return hip_status(nabla::launch_mask_build(g, geom->dtype == NABLA_DTYPE_BF16, q, k, qbar, kbar,
+                                             thr, win, mask_bits, row_count, adaptive_bits,
+                                             row_ptr, col_idx, as_stream(stream)));
+}
+
 int nabla_attn_fwd(const nabla_geom* geom, const void* q, const void* k, const void* v,
                    const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
                    void* stream) {
@@ -367,9 +388,8 @@ int nabla_forward(const nabla_geom* geom, const void* q, const void* k, const vo
   int32_t* ci = (int32_t*)(ws + off[5]);
   const hipStream_t s = as_stream(stream);
   const bool out_bf16 = geom->out_dtype == NABLA_DTYPE_BF16;
-  hipError_t e = nabla::launch_pool(g, bf16, q, k, qbar, kbar, s);
-  if (e == hipSuccess) e = nabla::launch_mask(g, qbar, kbar, thr, win, bits, cnt, nullptr, s);
-  if (e == hipSuccess) e = nabla::launch_compact(g, bits, cnt, rp, ci, s);
+  hipError_t e = nabla::launch_mask_build(g, bf16, q, k, qbar, kbar, thr, win, bits, cnt, nullptr,
+                                          rp, ci, s);
   if (bf16) {
     void* vt = ws + off[6];
     if (e == hipSuccess) e = nabla::launch_transpose_v(g, v, vt, s);

@@ -51,10 +51,6 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, soff, 0, 0);
 #endif
 }
-// Raw buffer descriptor over n bytes at p (gfx9 word 3: 32-bit data format).
-__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t n) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
-}
 
 // Ascending list of one row of a CSR structure (a query block's kept key
 // blocks, or a key block's query blocks in the transposed mask), read through

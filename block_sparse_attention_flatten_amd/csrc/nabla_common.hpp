@@ -62,6 +62,12 @@ __host__ __device__ inline BlockCoord block_coord(const Geo& g, int b) {
   return c;
 }
 
+// Raw buffer descriptor over n bytes at p (gfx9 word 3: 32-bit data format).
+// Loads at byte offsets >= n return zeros.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
 // Valid rows / columns of block b's 8 x 8 patch (8 unless it overhangs the latent edge).
 __device__ inline int block_rows_valid(const Geo& g, const BlockCoord& c) {
   const int r = g.H - c.hb * kP;
@@ -98,6 +104,11 @@ hipError_t launch_mask(const Geo& g, const float* qbar, const float* kbar, float
                        hipStream_t s);
 hipError_t launch_compact(const Geo& g, const uint32_t* bits, const int32_t* cnt,
                           int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
+// pool + mask + compact fused into a few launches (mask.hip)
+hipError_t launch_mask_build(const Geo& g, bool bf16, const void* q, const void* k, float* qbar,
+                             float* kbar, float thr, const int sta[3], uint32_t* bits,
+                             int32_t* cnt, uint32_t* abits, int32_t* row_ptr, int32_t* col_idx,
+                             hipStream_t s);
 // lse (nullable): float32 [bh, nb, 64] natural-log log-sum-exp of each query's
 // scaled scores over its kept valid keys; -inf for pad slots and empty rows
 hipError_t launch_attn_fwd(const Geo& g, bool bf16, bool out_bf16, const void* q, const void* k,

@@ -19,7 +19,8 @@
  *   nabla_transpose_v V in the per-block transposed operand layout
  *   nabla_attn_fwd_vt nabla_attn_fwd reading that layout (faster)
  *   nabla_unflatten   inverse reorder of the output
- *   nabla_forward     pool -> mask -> compact -> (transpose_v) -> attn_fwd in one call
+ *   nabla_mask_build  pool + mask + compact in one call (same outputs)
+ *   nabla_forward     mask_build -> (transpose_v) -> attn_fwd in one call
  *
  * Gradients with the kept-block mask held fixed (training with NABLA:
  * [GZ] core contributions and experimental results 2, pre-training;
@@ -80,7 +81,7 @@
 extern "C" {
 #endif
 
-#define NABLA_ABI_VERSION 2
+#define NABLA_ABI_VERSION 3
 
 enum nabla_status {
   NABLA_OK = 0,
@@ -169,6 +170,19 @@ int nabla_compact(const nabla_geom* geom, const uint32_t* mask_bits,
                   const int32_t* row_count, int32_t* row_ptr, int32_t* col_idx,
                   void* stream);
 
+/* Mask construction in one call: nabla_pool, nabla_mask and nabla_compact
+ * in that order on `stream` ([GZ] Methodology, downsampling + reduced
+ * attention + CDF thresholding + hybrid integration with STA; [LS] sec. 5,
+ * compressed storage).  Writes exactly what those three calls write, bit for
+ * bit: qbar, kbar, mask_bits, row_count, adaptive_bits (optional, may be
+ * NULL), row_ptr and col_idx, with the shapes given there; q, k in geom's
+ * layout and dtype; thr and sta as for nabla_mask.  Arguments are checked
+ * before anything is enqueued.  No workspace. */
+int nabla_mask_build(const nabla_geom* geom, const void* q, const void* k, float thr,
+                     const int32_t* sta, float* qbar, float* kbar, uint32_t* mask_bits,
+                     int32_t* row_count, uint32_t* adaptive_bits, int32_t* row_ptr,
+                     int32_t* col_idx, void* stream);
+
 /* Block-sparse attention forward ([GZ] Methodology, expansion of the block
  * mask to token resolution; [LS] sec. 2, step 3): for each valid query token
  * i of block r, o_i = sum_j softmax_j(q_i . k_j * scale) v_j over the valid
@@ -255,7 +269,7 @@ int nabla_attn_bwd_dkdv(const nabla_geom* geom, const void* q, const void* k,
  * aligned. */
 int nabla_forward_workspace_size(const nabla_geom* geom, size_t* bytes, size_t* offsets);
 
-/* One NABLA attention call: nabla_pool, nabla_mask, nabla_compact and the
+/* One NABLA attention call: nabla_mask_build (pooling, mask, lists) and the
  * attention (bf16: nabla_transpose_v + nabla_attn_fwd_vt; float32:
  * nabla_attn_fwd) in sequence on `stream`, with the intermediates in
  * `workspace` (device memory of at least nabla_forward_workspace_size bytes,

@@ -49,13 +49,14 @@ def tol(dtype: torch.dtype):
 
 
 def run_pipeline(cfg: synth.Config, q, k, v, layout=nabla.LAYOUT_THW, thr=None, sta=None,
-                 out_dtype=torch.float32, also_bf16=False, attn="vt"):
-    """Run pool -> mask -> compact -> attention through the C ABI, one entry
-    point at a time.  For bf16 inputs the attention is, by default, the launch
-    sequence bench.py times (nabla_transpose_v + nabla_attn_fwd_vt); attn="tr"
-    selects nabla_attn_fwd.  The output is float32 by default (the kernel's
-    result before any rounding to bf16); with ``also_bf16`` the attention is
-    run a second time writing bf16 (o_bf16)."""
+                 out_dtype=torch.float32, also_bf16=False, attn="vt", fused=True):
+    """Run mask construction and attention through the C ABI.  By default the
+    launch sequence bench.py times: nabla_mask_build (pooling, mask and lists
+    fused) and, for bf16 inputs, nabla_transpose_v + nabla_attn_fwd_vt;
+    fused=False calls nabla_pool, nabla_mask and nabla_compact one by one,
+    attn="tr" selects nabla_attn_fwd.  The output is float32 by default (the
+    kernel's result before any rounding to bf16); with ``also_bf16`` the
+    attention is run a second time writing bf16 (o_bf16)."""
     g = geom_of(cfg, layout, out_dtype)
     thr = cfg.thr if thr is None else thr
     sta = cfg.sta if sta is None else sta
@@ -69,9 +70,12 @@ def run_pipeline(cfg: synth.Config, q, k, v, layout=nabla.LAYOUT_THW, thr=None, 
     rp = torch.empty((B * h, nb + 1), dtype=torch.int32, device=dev)
     ci = torch.empty((B * h, nb * nb), dtype=torch.int32, device=dev)
     o = torch.empty(q.shape, dtype=g.odtype, device=dev)
-    nabla.nabla_pool(g, q, k, qbar, kbar)
-    nabla.nabla_mask(g, qbar, kbar, thr, sta, bits, cnt, abits)
-    nabla.nabla_compact(g, bits, cnt, rp, ci)
+    if fused:
+        nabla.nabla_mask_build(g, q, k, thr, sta, qbar, kbar, bits, cnt, abits, rp, ci)
+    else:
+        nabla.nabla_pool(g, q, k, qbar, kbar)
+        nabla.nabla_mask(g, qbar, kbar, thr, sta, bits, cnt, abits)
+        nabla.nabla_compact(g, bits, cnt, rp, ci)
     use_vt = attn == "vt" and q.dtype == torch.bfloat16
     vt = None
     if use_vt:
@@ -141,3 +145,14 @@ def check_output(got: np.ndarray, ref: np.ndarray, dtype, label=""):
     assert err.max() <= max_abs and err.mean() <= mean_abs, (
         f"{label}: max|err| {err.max():.3e} mean|err| {err.mean():.3e}")
     return float(err.max()), float(err.mean())
+
+
+def gpu_mask_for_oracle(ref, union: np.ndarray) -> np.ndarray:
+    """The mask the oracle's attention is compared under: the oracle's own
+    mask, with the band rows where the GPU chose a different (valid) cut
+    replaced by the GPU's rows, so that every output row can be compared."""
+    m = ref["mask"].copy()
+    diff = (union != m).any(1)
+    assert not (diff & ~ref["band"]).any()
+    m[diff] = union[diff]
+    return m

@@ -8,8 +8,8 @@ import torch
 
 import oracle as O
 import synth
-from gpu_helpers import (check_bf16_rounding, check_mask_rows, check_output, f64, log, ogeom,
-                         oracle_mask, run_pipeline, unpack_bits)
+from gpu_helpers import (check_bf16_rounding, check_mask_rows, check_output, f64,
+                         gpu_mask_for_oracle, log, ogeom, oracle_mask, run_pipeline, unpack_bits)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -39,9 +39,13 @@ def _run(cfg, q, k, v, thr=None, sta=None, label=""):
         union = unpack_bits(res["bits"][0, h], nb)
         adapt = unpack_bits(res["abits"][0, h], nb)
         nbnd, ndf = check_mask_rows(union, adapt, ref, thr, f"{label} h{h}")
-        rows = [r for r in _sample_rows(cfg, nb) if not (union[r] != ref["mask"][r]).any()]
+        # sampled rows plus every band row where the GPU cut differently, those
+        # compared under the GPU's row
+        m = gpu_mask_for_oracle(ref, union)
+        rows = sorted(set(_sample_rows(cfg, nb)) | set(np.flatnonzero((m != ref["mask"]).any(1))
+                                                       .tolist()))
         ob = O.block_sparse_attention(O.flatten(qh, og), O.flatten(kh, og), O.flatten(vh, og),
-                                      ref["mask"], ref["valid"], rows=rows)
+                                      m, ref["valid"], rows=rows)
         got = O.flatten(f64(res["o"][0, h]), og)
         sel = np.zeros_like(ref["valid"])
         sel[rows] = ref["valid"][rows]
@@ -113,9 +117,7 @@ def _backward_sampled(cfg, n_rows, n_cols, label):
     union = unpack_bits(res["bits"][0, h], nb)
     adapt = unpack_bits(res["abits"][0, h], nb)
     check_mask_rows(union, adapt, ref, cfg.thr, f"{label} h{h}")
-    m = ref["mask"].copy()
-    band = (union != m).any(1)
-    m[band] = union[band]
+    m = gpu_mask_for_oracle(ref, union)
     valid = ref["valid"]
     qb, kb, vb, gb = (O.flatten(x, og) for x in (qh, kh, vh, gh))
     rng = np.random.default_rng([cfg.seed, 11])

@@ -10,7 +10,7 @@ import block_sparse_attention_flatten_amd as nabla
 import oracle as O
 import synth
 from gpu_helpers import (check_bf16_rounding, check_mask_rows, check_output, f64, geom_of,
-                         log, ogeom, oracle_mask, run_pipeline, unpack_bits)
+                         gpu_mask_for_oracle, log, ogeom, oracle_mask, run_pipeline, unpack_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -125,18 +125,40 @@ def test_mask_and_forward(case):
             for r in range(nb):
                 cols = ci[bh, rp[bh, r]:rp[bh, r + 1]]
                 assert np.array_equal(cols, np.flatnonzero(union[b, h, r])), (name, b, h, r)
-            # output: rows whose mask matches the oracle's, vs the oracle's attention
-            same = ~(union[b, h] != ref["mask"]).any(1)
-            rows = np.flatnonzero(same)
+            # output of every row vs the oracle's attention (band rows where the
+            # GPU cut differently: under the GPU's row)
+            m = gpu_mask_for_oracle(ref, union[b, h])
             ob = O.block_sparse_attention(O.flatten(qh, og), O.flatten(kh, og), O.flatten(vh, og),
-                                          ref["mask"], ref["valid"], rows=rows)
+                                          m, ref["valid"])
             got = O.flatten(f64(res["o"][b, h]), og)
-            sel = np.zeros_like(ref["valid"])
-            sel[rows] = ref["valid"][rows]
+            sel = ref["valid"]
             e = check_output(got[sel], ob[sel], cfg.torch_dtype, f"{name} b{b} h{h}")
             log(f"{name} b{b} h{h}: kept {union[b, h].mean():.3f} band {nbnd} "
                 f"diff {ndf} max|err| {e[0]:.2e} mean|err| {e[1]:.2e}")
     log(f"{name}: band rows {n_band}, differing rows {n_diff}")
+
+
+@pytest.mark.parametrize("layout", [nabla.LAYOUT_THW, nabla.LAYOUT_BLOCKED])
+def test_mask_build_equals_separate_calls(case, layout):
+    """nabla_mask_build (pooling, mask and lists fused) writes exactly what
+    nabla_pool, nabla_mask and nabla_compact write one by one."""
+    name, cfg, q, k, v = case
+    if layout == nabla.LAYOUT_BLOCKED:
+        g = geom_of(cfg)
+        blk = [torch.empty(g.tensor_shape(nabla.LAYOUT_BLOCKED), dtype=q.dtype, device="cuda")
+               for _ in range(3)]
+        for x, xb in zip((q, k, v), blk):
+            nabla.nabla_flatten(g, x, xb)
+        q, k, v = blk
+    a = run_pipeline(cfg, q, k, v, layout=layout, fused=True)
+    b = run_pipeline(cfg, q, k, v, layout=layout, fused=False)
+    for key in ("qbar", "kbar", "bits", "abits", "cnt", "rp"):
+        assert torch.equal(a[key].view(torch.int32), b[key].view(torch.int32)), (name, key)
+    nnz = a["cnt"].to(torch.int64).sum(-1).flatten()
+    for i in range(nnz.numel()):
+        n = int(nnz[i])
+        assert torch.equal(a["ci"][i, :n], b["ci"][i, :n]), (name, "ci", i)
+    assert torch.equal(a["o"].view(torch.int32), b["o"].view(torch.int32)), (name, "o")
 
 
 def test_attention_with_oracle_masks(case):
