@@ -62,6 +62,8 @@ SIGNATURES = {
     "nabla_forward_workspace_size": ([_G, _SZP, _SZP], ctypes.c_int),
     "nabla_forward": ([_G, _P, _P, _P, ctypes.c_float, _I32P, ctypes.c_float, _P, _P,
                        ctypes.c_size_t, _P], ctypes.c_int),
+    "nabla_forward_noalloc": ([_G, _P, _P, _P, ctypes.c_float, _I32P, ctypes.c_float, _P, _P],
+                              ctypes.c_int),
     "nabla_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "nabla_last_hip_error": ([], ctypes.c_int),
     "nabla_abi_version": ([], ctypes.c_int),

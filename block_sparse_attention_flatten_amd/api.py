@@ -25,7 +25,8 @@ __all__ = [
     "NablaError", "Geometry", "nabla_num_blocks", "nabla_flatten", "nabla_unflatten",
     "nabla_pool", "nabla_mask", "nabla_compact", "nabla_mask_build", "nabla_attn_fwd",
     "nabla_transpose_v",
-    "nabla_attn_fwd_vt", "nabla_forward_workspace_size", "nabla_forward", "nabla_status_string",
+    "nabla_attn_fwd_vt", "nabla_forward_workspace_size", "nabla_forward", "nabla_forward_noalloc",
+    "nabla_status_string",
     "nabla_attn_fwd_lse", "nabla_attn_fwd_vt_lse", "nabla_mask_transpose", "nabla_attn_bwd_dq",
     "nabla_attn_bwd_dkdv", "forward", "backward", "vt_shape", "lse_shape",
     "LAYOUT_THW", "LAYOUT_BLOCKED",
@@ -328,6 +329,15 @@ def nabla_forward(g: Geometry, q, k, v, thr: float, sta, scale: float, o, worksp
         _ptr(v, "v", shp, g.dtype), float(thr), _sta(sta), float(scale),
         _ptr(o, "o", shp, g.odtype), _ptr(workspace, "workspace", None, torch.uint8),
         workspace.numel(), _stream(stream)), "nabla_forward")
+
+
+def nabla_forward_noalloc(g: Geometry, q, k, v, thr: float, sta, scale: float, o,
+                          stream=None) -> None:
+    shp = g.tensor_shape()
+    _check(_lib.load().nabla_forward_noalloc(
+        ctypes.byref(g.c()), _ptr(q, "q", shp, g.dtype), _ptr(k, "k", shp, g.dtype),
+        _ptr(v, "v", shp, g.dtype), float(thr), _sta(sta), float(scale),
+        _ptr(o, "o", shp, g.odtype), _stream(stream)), "nabla_forward_noalloc")
 
 
 # ---------------------------------------------------------------------------

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/nabla.h"
 #include "nabla_common.hpp"
 
@@ -102,6 +104,53 @@ void workspace_parts(const Geo& g, bool bf16, size_t off[kWsParts], size_t* tota
 
 hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
+// Checks shared by the two whole-call entry points, in the order nabla_forward
+// documents; NABLA_OK with g->bh == 0 means nothing to do.
+int check_forward(const nabla_geom* geom, const void* q, const void* k, const void* v, float thr,
+                  const int32_t* sta, float scale, const void* o, Geo* g, int win[3]) {
+  bool empty;
+  int st = make_geo(geom, true, g, &empty);
+  if (st != NABLA_OK) return st;
+  if (!scale_ok(scale)) return NABLA_E_SCALE;
+  st = check_sta(sta, win);
+  if (st != NABLA_OK) return st;
+  if (!thr_ok(thr, win)) return NABLA_E_THR;
+  if (empty) return NABLA_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return NABLA_E_NULL;
+  return NABLA_OK;
+}
+
+// One pass of the whole call over the heads of g, with its workspace parts at
+// ws + off[i]: mask construction, then the attention (bf16: through V^T).
+hipError_t forward_pass(const Geo& g, bool bf16, bool out_bf16, const void* q, const void* k,
+                        const void* v, float thr, const int win[3], float scale, void* o,
+                        char* ws, const size_t off[kWsParts], hipStream_t s) {
+  float* qbar = (float*)(ws + off[0]);
+  float* kbar = (float*)(ws + off[1]);
+  uint32_t* bits = (uint32_t*)(ws + off[2]);
+  int32_t* cnt = (int32_t*)(ws + off[3]);
+  int32_t* rp = (int32_t*)(ws + off[4]);
+  int32_t* ci = (int32_t*)(ws + off[5]);
+  hipError_t e = nabla::launch_mask_build(g, bf16, q, k, qbar, kbar, thr, win, bits, cnt, nullptr,
+                                          rp, ci, s);
+  if (bf16) {
+    void* vt = ws + off[6];
+    if (e == hipSuccess) e = nabla::launch_transpose_v(g, v, vt, s);
+    if (e == hipSuccess)
+      e = nabla::launch_attn_fwd_vt(g, out_bf16, q, k, vt, rp, ci, scale, o, nullptr, s);
+  } else if (e == hipSuccess) {
+    e = nabla::launch_attn_fwd(g, false, false, q, k, v, rp, ci, scale, o, nullptr, s);
+  }
+  return e;
+}
+
+// Device address of this GPU's copy of `scratch` (defined below), looked up
+// once per device with that device current and kept per device.
+constexpr int kMaxDevices = 64;
+std::atomic<char*> g_scratch_ptr[kMaxDevices];
+
+int scratch_of_current_device(char** out);
+
 int attn_fwd_impl(const nabla_geom* geom, const void* q, const void* k, const void* v,
                   const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
                   float* lse, bool need_lse, void* stream) {
@@ -134,6 +183,35 @@ int attn_fwd_vt_impl(const nabla_geom* geom, const void* q, const void* k, const
     return NABLA_E_NULL;
   return hip_status(nabla::launch_attn_fwd_vt(g, geom->out_dtype == NABLA_DTYPE_BF16, q, k, vt,
                                               row_ptr, col_idx, scale, o, lse, as_stream(stream)));
+}
+
+}  // namespace
+
+// Workspace of nabla_forward_noalloc: a file-scope device array, one copy on
+// every GPU the library runs on, held until the process ends.  On the host
+// the name `scratch` stands for a host-side shadow, not device memory, so
+// host code never passes it to a kernel or a copy: it uses the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[NABLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+int scratch_of_current_device(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return hip_status(hipErrorInvalidDevice);
+  char* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (addr == nullptr) return hip_status(hipErrorInvalidSymbol);
+    p = (char*)addr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return NABLA_OK;
 }
 
 }  // namespace
@@ -364,41 +442,55 @@ int nabla_forward(const nabla_geom* geom, const void* q, const void* k, const vo
                   const int32_t* sta, float scale, void* o, void* workspace,
                   size_t workspace_bytes, void* stream) {
   Geo g;
-  bool empty;
-  int st = make_geo(geom, true, &g, &empty);
-  if (st != NABLA_OK) return st;
-  if (!scale_ok(scale)) return NABLA_E_SCALE;
   int win[3];
-  st = check_sta(sta, win);
-  if (st != NABLA_OK) return st;
-  if (!thr_ok(thr, win)) return NABLA_E_THR;
-  if (empty) return NABLA_OK;
-  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || workspace == nullptr)
-    return NABLA_E_NULL;
+  int st = check_forward(geom, q, k, v, thr, sta, scale, o, &g, win);
+  if (st != NABLA_OK || g.bh == 0) return st;
+  if (workspace == nullptr) return NABLA_E_NULL;
   const bool bf16 = geom->dtype == NABLA_DTYPE_BF16;
   size_t off[kWsParts], total;
   workspace_parts(g, bf16, off, &total);
   if (workspace_bytes < total) return NABLA_E_WORKSPACE;
-  char* ws = (char*)workspace;
-  float* qbar = (float*)(ws + off[0]);
-  float* kbar = (float*)(ws + off[1]);
-  uint32_t* bits = (uint32_t*)(ws + off[2]);
-  int32_t* cnt = (int32_t*)(ws + off[3]);
-  int32_t* rp = (int32_t*)(ws + off[4]);
-  int32_t* ci = (int32_t*)(ws + off[5]);
-  const hipStream_t s = as_stream(stream);
+  return hip_status(forward_pass(g, bf16, geom->out_dtype == NABLA_DTYPE_BF16, q, k, v, thr, win,
+                                 scale, o, (char*)workspace, off, as_stream(stream)));
+}
+
+int nabla_forward_noalloc(const nabla_geom* geom, const void* q, const void* k, const void* v,
+                          float thr, const int32_t* sta, float scale, void* o, void* stream) {
+  Geo g;
+  int win[3];
+  int st = check_forward(geom, q, k, v, thr, sta, scale, o, &g, win);
+  if (st != NABLA_OK || g.bh == 0) return st;
+  const bool bf16 = geom->dtype == NABLA_DTYPE_BF16;
   const bool out_bf16 = geom->out_dtype == NABLA_DTYPE_BF16;
-  hipError_t e = nabla::launch_mask_build(g, bf16, q, k, qbar, kbar, thr, win, bits, cnt, nullptr,
-                                          rp, ci, s);
-  if (bf16) {
-    void* vt = ws + off[6];
-    if (e == hipSuccess) e = nabla::launch_transpose_v(g, v, vt, s);
-    if (e == hipSuccess)
-      e = nabla::launch_attn_fwd_vt(g, out_bf16, q, k, vt, rp, ci, scale, o, nullptr, s);
-  } else if (e == hipSuccess) {
-    e = nabla::launch_attn_fwd(g, false, false, q, k, v, rp, ci, scale, o, nullptr, s);
+  // heads per pass: as many as the scratch holds (at least one, else reject)
+  size_t off[kWsParts], total;
+  Geo gc = g;
+  gc.bh = 1;
+  workspace_parts(gc, bf16, off, &total);
+  if (total > (size_t)NABLA_NOALLOC_SCRATCH_BYTES) return NABLA_E_WORKSPACE;
+  int64_t per_pass = (int64_t)((size_t)NABLA_NOALLOC_SCRATCH_BYTES / total);
+  if (per_pass > g.bh) per_pass = g.bh;
+  for (;;) {                         // per-part alignment can add a few bytes per pass
+    gc.bh = per_pass;
+    workspace_parts(gc, bf16, off, &total);
+    if (total <= (size_t)NABLA_NOALLOC_SCRATCH_BYTES || per_pass == 1) break;
+    --per_pass;
   }
-  return hip_status(e);
+  char* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != NABLA_OK) return st;
+  const size_t in_head = (size_t)g.head_elems * (bf16 ? 2 : 4);
+  const size_t out_head = (size_t)g.head_elems * (out_bf16 ? 2 : 4);
+  const hipStream_t s = as_stream(stream);
+  for (int64_t h0 = 0; h0 < g.bh; h0 += per_pass) {
+    gc.bh = g.bh - h0 < per_pass ? g.bh - h0 : per_pass;
+    workspace_parts(gc, bf16, off, &total);
+    const hipError_t e = forward_pass(
+        gc, bf16, out_bf16, (const char*)q + h0 * in_head, (const char*)k + h0 * in_head,
+        (const char*)v + h0 * in_head, thr, win, scale, (char*)o + h0 * out_head, ws, off, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return NABLA_OK;
 }
 
 }  // extern "C"

@@ -21,6 +21,7 @@
  *   nabla_unflatten   inverse reorder of the output
  *   nabla_mask_build  pool + mask + compact in one call (same outputs)
  *   nabla_forward     mask_build -> (transpose_v) -> attn_fwd in one call
+ *   nabla_forward_noalloc  the same on a library-owned scratch array
  *
  * Gradients with the kept-block mask held fixed (training with NABLA:
  * [GZ] core contributions and experimental results 2, pre-training;
@@ -277,6 +278,26 @@ int nabla_forward_workspace_size(const nabla_geom* geom, size_t* bytes, size_t* 
 int nabla_forward(const nabla_geom* geom, const void* q, const void* k, const void* v,
                   float thr, const int32_t* sta, float scale, void* o,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* nabla_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments and results as nabla_forward, minus the workspace: the call
+ * uses a library-owned device array of NABLA_NOALLOC_SCRATCH_BYTES, one copy
+ * per GPU, created with the library's code on that GPU and held until the
+ * process ends, and allocates nothing.  Heads are processed in passes of as
+ * many heads as that array holds (the parts listed for
+ * nabla_forward_workspace_size, per pass), so the outputs equal
+ * nabla_forward's bit for bit.  Its device address is looked up on the first
+ * call on each device.  No part of the array needs to start at zero.
+ * Every call on one GPU shares that GPU's array and leaves its contents to
+ * the next: calls that overlap on one GPU (other streams, other threads)
+ * race, so serialize them.  Returns NABLA_E_WORKSPACE if one head's parts
+ * exceed the array (not reached below NABLA_MAX_BLOCKS at head_dim <= 128),
+ * other statuses as nabla_forward. */
+#define NABLA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int nabla_forward_noalloc(const nabla_geom* geom, const void* q, const void* k,
+                          const void* v, float thr, const int32_t* sta, float scale,
+                          void* o, void* stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* nabla_status_string(int status);

@@ -51,8 +51,8 @@ def tol(dtype: torch.dtype):
 def run_pipeline(cfg: synth.Config, q, k, v, layout=nabla.LAYOUT_THW, thr=None, sta=None,
                  out_dtype=torch.float32, also_bf16=False, attn="vt", fused=True):
     """Run mask construction and attention through the C ABI.  By default the
-    launch sequence bench.py times: nabla_mask_build (pooling, mask and lists
-    fused) and, for bf16 inputs, nabla_transpose_v + nabla_attn_fwd_vt;
+    launch sequence bench.py times: nabla_mask_build (pooling, mask and
+    lists in one call) and, for bf16 inputs, nabla_transpose_v + nabla_attn_fwd_vt;
     fused=False calls nabla_pool, nabla_mask and nabla_compact one by one,
     attn="tr" selects nabla_attn_fwd.  The output is float32 by default (the
     kernel's result before any rounding to bf16); with ``also_bf16`` the

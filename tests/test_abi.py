@@ -102,6 +102,14 @@ def test_argument_validation():
                              size.value, None) == -1
     assert lib.nabla_forward(ctypes.byref(g), FAKE, FAKE, FAKE, 2.0, None, 0.125, FAKE, FAKE,
                              size.value, None) == -6
+    assert lib.nabla_forward_noalloc(ctypes.byref(g), FAKE, FAKE, None, 0.5, None, 0.125, FAKE,
+                                     None) == -1
+    assert lib.nabla_forward_noalloc(ctypes.byref(g), FAKE, FAKE, FAKE, 2.0, None, 0.125, FAKE,
+                                     None) == -6
+    assert lib.nabla_forward_noalloc(ctypes.byref(g), FAKE, FAKE, FAKE, 0.5, None, -1.0, FAKE,
+                                     None) == -11
+    assert lib.nabla_forward_noalloc(ctypes.byref(G(head_dim=96)), FAKE, FAKE, FAKE, 0.5, None,
+                                     0.125, FAKE, None) == -4
 
 
 def test_empty_calls_launch_nothing():
@@ -114,6 +122,8 @@ def test_empty_calls_launch_nothing():
         assert lib.nabla_mask(ctypes.byref(g), None, None, 0.5, None, None, None, None, None) == 0
         assert lib.nabla_forward(ctypes.byref(g), None, None, None, 0.5, None, 0.1, None, None, 0,
                                  None) == 0
+        assert lib.nabla_forward_noalloc(ctypes.byref(g), None, None, None, 0.5, None, 0.1, None,
+                                         None) == 0
 
 
 def test_workspace_layout_and_block_count():
