@@ -366,6 +366,20 @@ int nabla_attn_fwd_vt(const nabla_geom* geom, const void* q, const void* k, cons
   return attn_fwd_vt_impl(geom, q, k, vt, row_ptr, col_idx, scale, o, nullptr, false, stream);
 }
 
+int nabla_dense_attn_fwd(const nabla_geom* geom, const void* q, const void* k, const void* vt,
+                         float scale, void* o, float* lse, void* stream) {
+  Geo g;
+  bool empty;
+  const int st = make_geo(geom, true, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (geom->dtype != NABLA_DTYPE_BF16) return NABLA_E_DTYPE;
+  if (!scale_ok(scale)) return NABLA_E_SCALE;
+  if (empty) return NABLA_OK;
+  if (q == nullptr || k == nullptr || vt == nullptr || o == nullptr) return NABLA_E_NULL;
+  return hip_status(nabla::launch_attn_dense_vt(g, geom->out_dtype == NABLA_DTYPE_BF16, q, k, vt,
+                                                scale, o, lse, as_stream(stream)));
+}
+
 int nabla_attn_fwd_vt_lse(const nabla_geom* geom, const void* q, const void* k, const void* vt,
                           const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
                           float* lse, void* stream) {

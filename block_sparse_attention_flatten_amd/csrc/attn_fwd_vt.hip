@@ -60,15 +60,15 @@ namespace {
 //    and 128 bytes of padding after every 8 rows move rows 8-15 into the other
 //    half of the banks.  Each 8-row group is 2 KB contiguous, so tiles still
 //    fill in whole 1-KB direct loads.
-template <int D>
+template <int D, int NW>
 struct VtShape {
   static constexpr bool kWideK = D == 128;             // 256-byte K rows
   static constexpr int kKGroupBytes = kWideK ? 8 * 256 + 128 : 8 * 128;
   static constexpr int kKBytes = 8 * kKGroupBytes;     // K tile in LDS
   static constexpr int kVBytes = D * kN * 2;           // V^T tile: d rows x 128 bytes
   static constexpr int kKChunks = D / 8;               // 16-byte chunks per K row
-  static constexpr int kKOps = kN * D * 2 / 1024 / 4;  // 1-KB direct loads per wavefront
-  static constexpr int kVOps = kVBytes / 1024 / 4;
+  static constexpr int kKOps = kN * D * 2 / 1024 / NW;  // 1-KB direct loads per wavefront
+  static constexpr int kVOps = kVBytes / 1024 / NW;
   static constexpr int kSteps = D / 16;                // k-steps of S^T = K Q^T
   static constexpr int kDTiles = D / 32;               // 32-row tiles of O^T
   static constexpr int kBufBytes = 2 * kKBytes + 2 * kVBytes;
@@ -94,13 +94,15 @@ __device__ inline float swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, typename OutT>
-__global__ void __launch_bounds__(256, 2)
+template <int D, typename OutT, int NW, bool kDense>
+__global__ void __launch_bounds__(NW * 64, 8 / NW)
 attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ VT, const int32_t* __restrict__ row_ptr,
                    const int32_t* __restrict__ col_idx, float scale_log2,
                    OutT* __restrict__ O, float* __restrict__ lse) {
-  using S = VtShape<D>;
+  static_assert(kDense || NW == 4, "the sparse walk serves pairs of query blocks");
+  constexpr int QB = NW / 2;         // query blocks per workgroup
+  using S = VtShape<D, NW>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   char* const kbuf = smem;                          // [2][kKBytes]
   char* const vbuf = smem + 2 * S::kKBytes;         // [2][kVBytes]
@@ -109,73 +111,88 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
   uint32_t* const bm = (uint32_t*)(smem + S::kBufBytes);   // [2][nw] bitmaps, then the count
   uint16_t* const ul = (uint16_t*)(bm + 2 * nw + 1);       // union list [nb]
 
-  const int items = pair_items(g);
+  const int items = kDense ? (nb + QB - 1) / QB : pair_items(g);
   int64_t head;
   int item;
   if (!xcd_item(blockIdx.x, items, (items + 7) >> 3, &head, &item)) return;
-  int qa, qpair;
-  pair_of(g, item, &qa, &qpair);
+  int qa = -1, qpair = -1;
+  if constexpr (!kDense) pair_of(g, item, &qa, &qpair);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 1;         // 0: first query block of the pair, 1: second
+  const int grp = wave >> 1;         // query block of the workgroup (sparse: of the pair)
   const int hl = lane >> 5;          // lane half
   const int jl = lane & 31;          // query column / operand row of this lane
-  const int myq = grp == 0 ? qa : qpair;   // -1: this wavefront only helps load
+  // -1: this wavefront only helps load
+  const int myq = kDense ? (QB * item + grp < nb ? QB * item + grp : -1)
+                         : (grp == 0 ? qa : qpair);
   const int64_t hoff = head * (int64_t)g.head_elems;
   const int row_step = block_row_step(g);
 
-  // ---- merged schedule: LDS bitmaps of both lists -> ascending union ----
-  for (int w = tid; w < 2 * nw; w += 256) bm[w] = 0u;
-  __syncthreads();
-  {
-    const int32_t* rp = row_ptr + head * (nb + 1);
-    const int32_t* cols = col_idx + head * (int64_t)nb * nb;
-#pragma unroll
-    for (int l = 0; l < 2; ++l) {
-      const int q = l == 0 ? qa : qpair;
-      if (q < 0) continue;
-      const int begin = rp[q], end = rp[q + 1];
-      if (begin < 0 || end < begin || end > nb * nb) continue;   // malformed row: no keys
-      for (int i = begin + tid; i < end; i += 256) {
-        const int c = cols[i];
-        if ((unsigned)c < (unsigned)nb) atomicOr(&bm[l * nw + (c >> 5)], 1u << (c & 31));
+  if constexpr (kDense) {
+    // ---- every key block, in order ----
+    for (int j = tid; j < nb; j += NW * 64) {
+      const BlockCoord c = block_coord(g, j);
+      const bool edge = block_rows_valid(g, c) < kP || block_cols_valid(g, c) < kP;
+      ul[j] = (uint16_t)(j | ((int)edge << 12) | (3 << 14));
+    }
+    if (tid == 0) bm[2 * nw] = (uint32_t)nb;
+    __syncthreads();
+  } else {
+    // ---- merged schedule: LDS bitmaps of both lists -> ascending union ----
+    for (int w = tid; w < 2 * nw; w += NW * 64) bm[w] = 0u;
+    __syncthreads();
+    {
+      const int32_t* rp = row_ptr + head * (nb + 1);
+      const int32_t* cols = col_idx + head * (int64_t)nb * nb;
+  #pragma unroll
+      for (int l = 0; l < 2; ++l) {
+        const int q = l == 0 ? qa : qpair;
+        if (q < 0) continue;
+        const int begin = rp[q], end = rp[q + 1];
+        if (begin < 0 || end < begin || end > nb * nb) continue;   // malformed row: no keys
+        for (int i = begin + tid; i < end; i += NW * 64) {
+          const int c = cols[i];
+          if ((unsigned)c < (unsigned)nb) atomicOr(&bm[l * nw + (c >> 5)], 1u << (c & 31));
+        }
       }
     }
-  }
-  __syncthreads();
-  if (wave == 0) {                   // nw <= 128: two words per lane
-    const int w0 = 2 * lane, w1 = w0 + 1;
-    const uint32_t a0 = w0 < nw ? bm[w0] : 0u, b0 = w0 < nw ? bm[nw + w0] : 0u;
-    const uint32_t a1 = w1 < nw ? bm[w1] : 0u, b1 = w1 < nw ? bm[nw + w1] : 0u;
-    const int cnt = __popc(a0 | b0) + __popc(a1 | b1);
-    int incl = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
-    int pos = incl - cnt;
-    auto expand = [&](uint32_t a, uint32_t b, int w) {
-      uint32_t u = a | b;
-      while (u) {
-        const int bit = __builtin_ctz(u);
-        u &= u - 1;
-        const int blk = (w << 5) | bit;
-        const BlockCoord c = block_coord(g, blk);
-        const bool edge = block_rows_valid(g, c) < kP || block_cols_valid(g, c) < kP;
-        ul[pos++] = (uint16_t)(blk | ((int)edge << 12) | (((a >> bit) & 1u) << 14) |
-                               (((b >> bit) & 1u) << 15));
+    __syncthreads();
+    if (wave == 0) {                   // nw <= 128: two words per lane
+      const int w0 = 2 * lane, w1 = w0 + 1;
+      const uint32_t a0 = w0 < nw ? bm[w0] : 0u, b0 = w0 < nw ? bm[nw + w0] : 0u;
+      const uint32_t a1 = w1 < nw ? bm[w1] : 0u, b1 = w1 < nw ? bm[nw + w1] : 0u;
+      const int cnt = __popc(a0 | b0) + __popc(a1 | b1);
+      int incl = cnt;
+  #pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
       }
-    };
-    expand(a0, b0, w0);
-    expand(a1, b1, w1);
-    if (lane == 63) bm[2 * nw] = (uint32_t)incl;
+      int pos = incl - cnt;
+      auto expand = [&](uint32_t a, uint32_t b, int w) {
+        uint32_t u = a | b;
+        while (u) {
+          const int bit = __builtin_ctz(u);
+          u &= u - 1;
+          const int blk = (w << 5) | bit;
+          const BlockCoord c = block_coord(g, blk);
+          const bool edge = block_rows_valid(g, c) < kP || block_cols_valid(g, c) < kP;
+          ul[pos++] = (uint16_t)(blk | ((int)edge << 12) | (((a >> bit) & 1u) << 14) |
+                                 (((b >> bit) & 1u) << 15));
+        }
+      };
+      expand(a0, b0, w0);
+      expand(a1, b1, w1);
+      if (lane == 63) bm[2 * nw] = (uint32_t)incl;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   const int U = __builtin_amdgcn_readfirstlane((int)bm[2 * nw]);
   const int mine_bit = 14 + grp;     // flag of this wavefront's query block in an entry
+  // does this wavefront's query block keep the entry's key block
+  auto mine = [&](int e) { return kDense ? e >= 0 : e >= 0 && ((e >> mine_bit) & 1); };
   auto entry = [&](int j) -> int {   // wave-uniform schedule entry, -1 past the end
     return j < U ? __builtin_amdgcn_readfirstlane((int)ul[j]) : -1;
   };
@@ -224,7 +241,7 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
     kdma_lane[par] = (r & 7) * D + c * 8;
   }
   auto kdma_rows = [&](int i) {     // 8-row group of op i (wavefront-uniform)
-    return S::kWideK ? 2 * wave + (i >> 1) : 2 * wave + i;
+    return S::kWideK ? (S::kKOps / 2) * wave + (i >> 1) : S::kKOps * wave + i;
   };
   auto kdma_full = [&](int i) { return kdma_rows(i) * row_step + kdma_lane[i & 1]; };
   // V^T op o: rows 8o + lane / 8, logical chunk (lane % 8) ^ g(row); g's
@@ -449,7 +466,7 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
   }
   wait_vmcnt0();
   __builtin_amdgcn_s_barrier();
-  if (e0 >= 0 && ((e0 >> mine_bit) & 1)) {
+  if (mine(e0)) {
     bf16x8 ka[2][S::kSteps];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -475,8 +492,8 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
     const int e3v = s + 3 < U ? (int)ul[s + 3] : -1;   // made uniform at the end
     if (e2 >= 0) load_k(e2, kbuf + (s & 1) * S::kKBytes);
     if (e1 >= 0) load_v(e1, vbuf + ((s + 1) & 1) * S::kVBytes);
-    const bool do_b = (e0 >> mine_bit) & 1;
-    const bool do_a = e1 >= 0 && ((e1 >> mine_bit) & 1);
+    const bool do_b = mine(e0);
+    const bool do_a = mine(e1);
     if (do_b) stage_b_pre(sc, e0);
     const int kb = ((s + 1) & 1) * S::kKBytes;   // buffer offsets within the K / V^T areas
     const int vb = (s & 1) * S::kVBytes;
@@ -520,24 +537,28 @@ attn_fwd_vt_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __re
   }
 }
 
-template <int D, typename OutT>
+template <int D, typename OutT, int NW, bool kDense>
 hipError_t launch_vt(const Geo& g, const void* q, const void* k, const void* vt,
                      const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
                      float* lse, hipStream_t s) {
-  using S = VtShape<D>;
+  using S = VtShape<D, NW>;
   const int nw = (g.nb + 31) >> 5;
   const size_t lds = S::kBufBytes + (size_t)(2 * nw + 1) * 4 + (size_t)g.nb * 2;
-  auto kern = attn_fwd_vt_kernel<D, OutT>;
+  auto kern = attn_fwd_vt_kernel<D, OutT, NW, kDense>;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const float sl2 = scale * 1.4426950408889634f;   // exp(x) = exp2(x log2 e)
-  const int64_t chunk = (pair_items(g) + 7) / 8;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(8 * chunk * g.bh)), dim3(256), lds, s, g,
+  const int64_t items = kDense ? (g.nb + NW / 2 - 1) / (NW / 2) : pair_items(g);
+  const int64_t chunk = (items + 7) / 8;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(8 * chunk * g.bh)), dim3(NW * 64), lds, s, g,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)vt, row_ptr, col_idx,
                      sl2, (OutT*)o, lse);
   return hipGetLastError();
 }
+
+// dense: four query blocks per workgroup (eight wavefronts), every key block
+constexpr int kDenseWaves = 8;
 
 }  // namespace
 
@@ -545,10 +566,25 @@ hipError_t launch_attn_fwd_vt(const Geo& g, bool out_bf16, const void* q, const 
                               const void* vt, const int32_t* row_ptr, const int32_t* col_idx,
                               float scale, void* o, float* lse, hipStream_t s) {
   if (g.d == 64)
-    return out_bf16 ? launch_vt<64, __bf16>(g, q, k, vt, row_ptr, col_idx, scale, o, lse, s)
-                    : launch_vt<64, float>(g, q, k, vt, row_ptr, col_idx, scale, o, lse, s);
-  return out_bf16 ? launch_vt<128, __bf16>(g, q, k, vt, row_ptr, col_idx, scale, o, lse, s)
-                  : launch_vt<128, float>(g, q, k, vt, row_ptr, col_idx, scale, o, lse, s);
+    return out_bf16
+               ? launch_vt<64, __bf16, 4, false>(g, q, k, vt, row_ptr, col_idx, scale, o, lse, s)
+               : launch_vt<64, float, 4, false>(g, q, k, vt, row_ptr, col_idx, scale, o, lse, s);
+  return out_bf16
+             ? launch_vt<128, __bf16, 4, false>(g, q, k, vt, row_ptr, col_idx, scale, o, lse, s)
+             : launch_vt<128, float, 4, false>(g, q, k, vt, row_ptr, col_idx, scale, o, lse, s);
+}
+
+hipError_t launch_attn_dense_vt(const Geo& g, bool out_bf16, const void* q, const void* k,
+                                const void* vt, float scale, void* o, float* lse,
+                                hipStream_t s) {
+  constexpr int NW = kDenseWaves;
+  if (g.d == 64)
+    return out_bf16
+               ? launch_vt<64, __bf16, NW, true>(g, q, k, vt, nullptr, nullptr, scale, o, lse, s)
+               : launch_vt<64, float, NW, true>(g, q, k, vt, nullptr, nullptr, scale, o, lse, s);
+  return out_bf16
+             ? launch_vt<128, __bf16, NW, true>(g, q, k, vt, nullptr, nullptr, scale, o, lse, s)
+             : launch_vt<128, float, NW, true>(g, q, k, vt, nullptr, nullptr, scale, o, lse, s);
 }
 
 }  // namespace nabla

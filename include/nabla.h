@@ -18,6 +18,7 @@
  *   nabla_attn_fwd    exact attention on kept N x N token blocks   [GZ] expansion; [LS] sec. 2
  *   nabla_transpose_v V in the per-block transposed operand layout
  *   nabla_attn_fwd_vt nabla_attn_fwd reading that layout (faster)
+ *   nabla_dense_attn_fwd  full attention (the baseline)   [GZ] experimental results 1
  *   nabla_unflatten   inverse reorder of the output
  *   nabla_mask_build  pool + mask + compact in one call (same outputs)
  *   nabla_forward     mask_build -> (transpose_v) -> attn_fwd in one call
@@ -211,6 +212,18 @@ int nabla_transpose_v(const nabla_geom* geom, const void* v, void* vt, void* str
 int nabla_attn_fwd_vt(const nabla_geom* geom, const void* q, const void* k,
                       const void* vt, const int32_t* row_ptr, const int32_t* col_idx,
                       float scale, void* o, void* stream);
+
+/* Dense (full) attention, the baseline that the method's speed-ups are
+ * measured against ([GZ] experimental results 1, speed-up over full
+ * attention; [LS] sec. 3, generation time against full attention): every
+ * valid query attends to every valid key of its head, with no mask and no
+ * kept lists.  bf16 inputs only (NABLA_E_DTYPE otherwise); q, k in geom's
+ * layout, vt from nabla_transpose_v; o in geom's layout and out_dtype; lse
+ * optional (may be NULL), float32 [B, heads, nb, 64] as for
+ * nabla_attn_fwd_lse.  Equal, up to float rounding order, to nabla_attn_fwd
+ * on the all-kept mask. */
+int nabla_dense_attn_fwd(const nabla_geom* geom, const void* q, const void* k,
+                         const void* vt, float scale, void* o, float* lse, void* stream);
 
 /* Gradients ([GZ] core contributions, "dual-stage acceleration" of training
  * and inference, and experimental results 2, pre-training a 2B DiT with

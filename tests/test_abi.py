@@ -92,6 +92,12 @@ def test_argument_validation():
                                  FAKE, 0.1, FAKE, None) == -3
     assert lib.nabla_attn_fwd_vt(ctypes.byref(g), FAKE, FAKE, None, FAKE, FAKE, 0.1, FAKE,
                                  None) == -1
+    assert lib.nabla_dense_attn_fwd(ctypes.byref(G(dtype=0, out_dtype=0)), FAKE, FAKE, FAKE, 0.1,
+                                    FAKE, None, None) == -3
+    assert lib.nabla_dense_attn_fwd(ctypes.byref(g), FAKE, FAKE, None, 0.1, FAKE, None,
+                                    None) == -1
+    assert lib.nabla_dense_attn_fwd(ctypes.byref(g), FAKE, FAKE, FAKE, 0.0, FAKE, None,
+                                    None) == -11
     assert lib.nabla_flatten(ctypes.byref(g), None, FAKE, None) == -1
     assert lib.nabla_unflatten(ctypes.byref(g), FAKE, None, None) == -1
     size = ctypes.c_size_t(0)

@@ -371,3 +371,60 @@ def test_out_of_range_list_entries_are_skipped(path):
     og = ogeom(cfg)
     last = O.flatten(f64(outs[1][0, 0]), og)[nb - 1][O.valid_tokens(og)[nb - 1]]
     assert np.all(last == 0)
+
+
+@pytest.mark.parametrize("layout", [nabla.LAYOUT_THW, nabla.LAYOUT_BLOCKED])
+def test_dense_attention(case, layout):
+    """nabla_dense_attn_fwd (no mask, no lists) against the oracle's attention
+    on the all-kept mask (pinned to textbook softmax attention), lse included;
+    and bit-equal to the sparse kernel walking the all-kept lists."""
+    name, cfg, q, k, v = case
+    if cfg.torch_dtype != torch.bfloat16:
+        pytest.skip("the dense kernel reads V^T (bf16 inputs only)")
+    g = geom_of(cfg, layout, out_dtype=torch.float32)
+    if layout == nabla.LAYOUT_BLOCKED:
+        qb, kb, vb = (torch.empty(g.tensor_shape(layout), dtype=q.dtype, device="cuda")
+                      for _ in range(3))
+        for src, dst in ((q, qb), (k, kb), (v, vb)):
+            nabla.nabla_flatten(geom_of(cfg), src, dst)
+        q, k, v = qb, kb, vb
+    nb = g.nb
+    bh = cfg.batch * cfg.heads
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    vt = torch.empty(nabla.vt_shape(g), dtype=q.dtype, device="cuda")
+    nabla.nabla_transpose_v(g, v, vt)
+    o = torch.full(g.tensor_shape(layout), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.empty(nabla.lse_shape(g), dtype=torch.float32, device="cuda")
+    nabla.nabla_dense_attn_fwd(g, q, k, vt, scale, o, lse)
+    # the sparse kernel over every block
+    rp = (torch.arange(nb + 1, dtype=torch.int32, device="cuda") * nb).repeat(bh, 1).contiguous()
+    ci = torch.arange(nb, dtype=torch.int32, device="cuda").repeat(bh, nb).contiguous()
+    o_sp = torch.empty_like(o)
+    lse_sp = torch.empty_like(lse)
+    nabla.nabla_attn_fwd_vt_lse(g, q, k, vt, rp, ci, scale, o_sp, lse_sp)
+    ob = torch.empty(g.tensor_shape(layout), dtype=torch.bfloat16, device="cuda")
+    gb = geom_of(cfg, layout, out_dtype=torch.bfloat16)
+    nabla.nabla_dense_attn_fwd(gb, q, k, vt, scale, ob, None)
+    torch.cuda.synchronize()
+    og = ogeom(cfg)
+    valid = O.valid_tokens(og)
+    full = np.ones((nb, nb), dtype=bool)
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            if layout == nabla.LAYOUT_THW:
+                qh, kh, vh = (O.flatten(f64(x[b, h]), og) for x in (q, k, v))
+                got = O.flatten(f64(o[b, h]), og)
+            else:
+                qh, kh, vh = (f64(x[b, h]).reshape(nb, 64, -1) for x in (q, k, v))
+                got = f64(o[b, h]).reshape(nb, 64, -1)
+            ref = O.block_sparse_attention(qh, kh, vh, full, valid)
+            check_output(got[valid], ref[valid], cfg.torch_dtype, f"{name} dense b{b} h{h}")
+            # lse against ln sum exp over every valid key
+            s = np.einsum("qd,kd->qk", qh[valid], kh[valid]) * scale
+            m = s.max(1, keepdims=True)
+            want = (m[:, 0] + np.log(np.exp(s - m).sum(1)))
+            assert np.abs(lse[b, h].cpu().numpy()[valid] - want).max() < 1e-2
+    assert torch.equal(o.view(torch.int32), o_sp.view(torch.int32)), name
+    assert torch.equal(lse.view(torch.int32), lse_sp.view(torch.int32)), name
+    # the bf16 output is the float32 result rounded to nearest even
+    assert torch.equal(ob.view(torch.int16), o.to(torch.bfloat16).view(torch.int16)), name
