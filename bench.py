@@ -59,12 +59,13 @@ def parse():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the gradient calls (dq, dk, dv with the mask held fixed)")
     ap.add_argument("--no-dense", action="store_true",
-                    help="skip the dense reference (the same kernel with every block kept)")
+                    help="skip the dense references (nabla_dense_attn_fwd, the sparse kernel "
+                         "with every block kept, torch flash SDPA)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
-    ap.add_argument("--layer", action="store_true",
-                    help="also time a Wan-shaped attention layer (QKV and output projections "
-                         "on hipBLASLt around the NABLA call, tokens in the blocked order)")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the Wan-shaped attention layer (QKV and output projections on "
+                         "hipBLASLt around the NABLA call, tokens in the blocked order)")
     ap.add_argument("--serial", action="store_true",
                     help="run every stage of the step on one stream (no V^T overlap)")
     ap.add_argument("--no-peaks", action="store_true",
@@ -189,11 +190,14 @@ def layer_leg(torch, nabla, cfg, g, x_field, thr, sta, scale, time_call, dev):
     """One self-attention layer of a Wan-shaped DiT around the NABLA call,
     with the token sequence kept in the blocked (fractal-flattened) order
     across the network, so no reorder runs per layer: X [S, h d] ->
-    QKV = X W_qkv (one hipBLASLt GEMM through torch.matmul) -> head-major
-    copies -> NABLA (pool, mask, compact, V^T, attention; blocked layout) ->
-    token-major copy -> O W_o.  Random weights; X is the bench's synthetic Q
-    field, reordered once; pad tokens of the blocked order are zero.  Same layer with torch's flash SDPA in place
-    of NABLA for comparison (tokens of the valid set only)."""
+    QKV = X W_qkv (one hipBLASLt GEMM through torch.matmul) ->
+    nabla_qkv_split (head-major q, k, V^T and the block means in one pass) ->
+    mask, lists, attention (blocked layout) -> token-major copy -> O W_o.
+    Random weights; X is the bench's synthetic Q field, reordered once; pad
+    tokens of the blocked order are zero.  Timed beside it: the same layer
+    with the separate passes the split replaces (head-major copy, nabla_pool,
+    nabla_transpose_v), and with torch's flash SDPA in place of NABLA (tokens
+    of the valid set only)."""
     from torch.nn.attention import SDPBackend, sdpa_kernel
     if cfg.torch_dtype != torch.bfloat16 or cfg.batch != 1:
         return None
@@ -219,19 +223,27 @@ def layer_leg(torch, nabla, cfg, g, x_field, thr, sta, scale, time_call, dev):
     rp = torch.empty((h, nb + 1), dtype=torch.int32, device=dev)
     ci = torch.empty((h, nb * nb), dtype=torch.int32, device=dev)
     vt = torch.empty(nabla.vt_shape(gb), dtype=torch.bfloat16, device=dev)
+    q = torch.empty(gb.tensor_shape(), dtype=torch.bfloat16, device=dev)
+    k = torch.empty_like(q)
+    o = torch.empty_like(q)
     st = {}
 
     def proj_in():
-        qkv = X @ Wqkv                            # [S, 3 h d]
-        st["qkv"] = qkv.view(S, 3, h, d).permute(1, 2, 0, 3).contiguous()   # [3, h, S, d]
+        st["qkv"] = torch.matmul(X, Wqkv).view(nabla.qkv_shape(gb))   # [1, S, 3, h, d]
+
+    def split():
+        nabla.nabla_qkv_split(gb, st["qkv"], q, k, vt, qbar, kbar)
+
+    def split_separate():                         # what the split replaces
+        hm = st["qkv"].permute(2, 0, 3, 1, 4).contiguous().view(3, *gb.tensor_shape())
+        nabla.nabla_pool(gb, hm[0], hm[1], qbar, kbar)
+        nabla.nabla_transpose_v(gb, hm[2], vt)
+        st["hm"] = hm
 
     def attention():
-        q, k, v = (st["qkv"][i].view(1, h, nb, 64, d) for i in range(3))
-        o = torch.empty_like(q)
-        nabla.nabla_pool(gb, q, k, qbar, kbar)
+        split()
         nabla.nabla_mask(gb, qbar, kbar, thr, sta, bits, cnt, None)
         nabla.nabla_compact(gb, bits, cnt, rp, ci)
-        nabla.nabla_transpose_v(gb, v, vt)
         nabla.nabla_attn_fwd_vt(gb, q, k, vt, rp, ci, scale, o)
         st["o"] = o
 
@@ -244,21 +256,25 @@ def layer_leg(torch, nabla, cfg, g, x_field, thr, sta, scale, time_call, dev):
         proj_out()
 
     layer()
-    ms = {"qkv_projection_and_head_major_copy": time_call(proj_in, reps=3),
-          "nabla_attention": time_call(attention, reps=3),
+    ms = {"qkv_projection": time_call(proj_in, reps=3),
+          "qkv_split_with_pooling": time_call(split, reps=3),
+          "nabla_attention_incl_split": time_call(attention, reps=3),
           "token_major_copy_and_output_projection": time_call(proj_out, reps=3),
           "layer": time_call(layer, reps=3)}
+    separate_ms = time_call(split_separate, reps=3)
+    st.pop("hm", None)
     # the same layer with dense flash attention over the valid tokens
     valid = torch.from_numpy(np.ascontiguousarray(valid_slots(cfg, nb))).to(dev)
-    sv = int(valid.sum())
 
     def dense_attention():
-        q, k, v = (st["qkv"][i][:, valid].unsqueeze(0) for i in range(3))   # [1, h, Sv, d]
+        qkv = st["qkv"][0]                        # [S, 3, h, d]
+        qd, kd, vd = (qkv[valid, i].permute(1, 0, 2).unsqueeze(0).contiguous()
+                      for i in range(3))          # [1, h, Sv, d]
         with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
-            od = torch.nn.functional.scaled_dot_product_attention(q, k, v)
-        o = torch.zeros((h, S, d), dtype=torch.bfloat16, device=dev)
-        o[:, valid] = od[0]
-        st["o"] = o
+            od = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd)
+        out = torch.zeros((h, S, d), dtype=torch.bfloat16, device=dev)
+        out[:, valid] = od[0]
+        st["o"] = out
 
     def dense_layer():
         proj_in()
@@ -274,15 +290,17 @@ def layer_leg(torch, nabla, cfg, g, x_field, thr, sta, scale, time_call, dev):
     torch.cuda.synchronize()
     sparsity = 1.0 - int(cnt.to(torch.int64).sum()) / (h * nb * nb)
     out = {"what": "Wan-shaped self-attention layer, tokens in the blocked order (flattened "
-                   "once per network): QKV projection, NABLA, output projection",
+                   "once per network): QKV projection, nabla_qkv_split (q, k, V^T, block "
+                   "means), mask + lists + attention, output projection",
            "tokens_blocked": S, "model_dim": D, "sparsity": round(sparsity, 4),
            "ms": {k_: round(v_, 3) for k_, v_ in ms.items()},
-           "attention_share": round(ms["nabla_attention"] / ms["layer"], 3),
+           "separate_copy_pool_transpose_ms": round(separate_ms, 3),
+           "attention_share": round(ms["nabla_attention_incl_split"] / ms["layer"], 3),
            "dense_flash_layer_ms": None if dense_ms is None else round(dense_ms, 3),
            "layer_speedup_vs_dense_flash": None if dense_ms is None
            else round(dense_ms / ms["layer"], 3)}
     log(f"dit layer: {out}")
-    del X, Wqkv, Wo, st
+    del X, Wqkv, Wo, st, q, k, o, vt
     return out
 
 
@@ -711,7 +729,7 @@ def main():
             tf["speedup_sparse_backward_vs_torch_flash"] = round(
                 tf["backward_ms"] / result["backward"]["ms"], 3)
         result["dense_reference"]["torch_sdpa_flash"] = tf
-    if args.layer:
+    if not args.no_layer:
         result["dit_layer"] = layer_leg(torch, nabla, cfg, g, q, thr, sta, scale, time_call, dev)
     if not args.no_cpu_baseline:
         step()                       # the call's own mask and output again (the legs above

@@ -52,6 +52,7 @@ SIGNATURES = {
     "nabla_transpose_v": ([_G, _P, _P, _P], ctypes.c_int),
     "nabla_attn_fwd_vt": ([_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P], ctypes.c_int),
     "nabla_dense_attn_fwd": ([_G, _P, _P, _P, ctypes.c_float, _P, _P, _P], ctypes.c_int),
+    "nabla_qkv_split": ([_G, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "nabla_attn_fwd_lse": ([_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P], ctypes.c_int),
     "nabla_attn_fwd_vt_lse": ([_G, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P],
                               ctypes.c_int),

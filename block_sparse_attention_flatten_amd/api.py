@@ -24,7 +24,7 @@ from ._lib import DTYPE_BF16, DTYPE_F32, LAYOUT_BLOCKED, LAYOUT_THW, nabla_geom
 __all__ = [
     "NablaError", "Geometry", "nabla_num_blocks", "nabla_flatten", "nabla_unflatten",
     "nabla_pool", "nabla_mask", "nabla_compact", "nabla_mask_build", "nabla_attn_fwd",
-    "nabla_transpose_v", "nabla_dense_attn_fwd",
+    "nabla_transpose_v", "nabla_dense_attn_fwd", "nabla_qkv_split", "qkv_shape",
     "nabla_attn_fwd_vt", "nabla_forward_workspace_size", "nabla_forward", "nabla_forward_noalloc",
     "nabla_status_string",
     "nabla_attn_fwd_lse", "nabla_attn_fwd_vt_lse", "nabla_mask_transpose", "nabla_attn_bwd_dq",
@@ -243,6 +243,22 @@ def nabla_attn_fwd_vt(g: Geometry, q, k, vt, row_ptr, col_idx, scale: float, o,
         _ptr(row_ptr, "row_ptr", (bh, g.nb + 1), torch.int32),
         _ptr(col_idx, "col_idx", (bh, g.nb * g.nb), torch.int32), float(scale),
         _ptr(o, "o", shp, g.odtype), _stream(stream)), "nabla_attn_fwd_vt")
+
+
+def qkv_shape(g: Geometry) -> Tuple[int, ...]:
+    """Shape of a fused QKV projection output in the blocked token order,
+    [B, nb * 64, 3, heads, d]."""
+    return (g.batch, g.nb * 64, 3, g.heads, g.head_dim)
+
+
+def nabla_qkv_split(g: Geometry, qkv, q, k, vt, qbar, kbar, stream=None) -> None:
+    shp = g.tensor_shape(LAYOUT_BLOCKED)
+    means = (g.batch, g.heads, g.nb, g.head_dim)
+    _check(_lib.load().nabla_qkv_split(
+        ctypes.byref(g.c()), _ptr(qkv, "qkv", qkv_shape(g), g.dtype),
+        _ptr(q, "q", shp, g.dtype), _ptr(k, "k", shp, g.dtype),
+        _ptr(vt, "vt", vt_shape(g), g.dtype), _ptr(qbar, "qbar", means, torch.float32),
+        _ptr(kbar, "kbar", means, torch.float32), _stream(stream)), "nabla_qkv_split")
 
 
 def nabla_dense_attn_fwd(g: Geometry, q, k, vt, scale: float, o, lse=None,

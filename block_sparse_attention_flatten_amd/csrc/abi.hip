@@ -366,6 +366,23 @@ int nabla_attn_fwd_vt(const nabla_geom* geom, const void* q, const void* k, cons
   return attn_fwd_vt_impl(geom, q, k, vt, row_ptr, col_idx, scale, o, nullptr, false, stream);
 }
 
+int nabla_qkv_split(const nabla_geom* geom, const void* qkv, void* q, void* k, void* vt,
+                    float* qbar, float* kbar, void* stream) {
+  Geo g;
+  bool empty;
+  const int st = make_geo(geom, true, &g, &empty);
+  if (st != NABLA_OK) return st;
+  if (geom->dtype != NABLA_DTYPE_BF16) return NABLA_E_DTYPE;
+  if (geom->layout != NABLA_LAYOUT_BLOCKED) return NABLA_E_LAYOUT;
+  if (geom->batch > 65535) return NABLA_E_SHAPE;    // one grid plane per batch entry
+  if (empty) return NABLA_OK;
+  if (qkv == nullptr || q == nullptr || k == nullptr || vt == nullptr || qbar == nullptr ||
+      kbar == nullptr)
+    return NABLA_E_NULL;
+  return hip_status(nabla::launch_qkv_split(g, (int)geom->batch, (int)geom->heads, qkv, q, k, vt,
+                                            qbar, kbar, as_stream(stream)));
+}
+
 int nabla_dense_attn_fwd(const nabla_geom* geom, const void* q, const void* k, const void* vt,
                          float scale, void* o, float* lse, void* stream) {
   Geo g;

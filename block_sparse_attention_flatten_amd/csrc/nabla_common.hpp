@@ -130,6 +130,8 @@ hipError_t launch_attn_bwd_dkdv(const Geo& g, bool bf16, const void* q, const vo
 hipError_t launch_attn_fwd_vt(const Geo& g, bool out_bf16, const void* q, const void* k,
                               const void* vt, const int32_t* row_ptr, const int32_t* col_idx,
                               float scale, void* o, float* lse, hipStream_t s);
+hipError_t launch_qkv_split(const Geo& g, int batch, int heads, const void* qkv, void* q, void* k,
+                            void* vt, float* qbar, float* kbar, hipStream_t s);
 hipError_t launch_attn_dense_vt(const Geo& g, bool out_bf16, const void* q, const void* k,
                                 const void* vt, float scale, void* o, float* lse,
                                 hipStream_t s);

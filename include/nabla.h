@@ -19,6 +19,7 @@
  *   nabla_transpose_v V in the per-block transposed operand layout
  *   nabla_attn_fwd_vt nabla_attn_fwd reading that layout (faster)
  *   nabla_dense_attn_fwd  full attention (the baseline)   [GZ] experimental results 1
+ *   nabla_qkv_split   QKV projection output -> q, k, V^T and block means
  *   nabla_unflatten   inverse reorder of the output
  *   nabla_mask_build  pool + mask + compact in one call (same outputs)
  *   nabla_forward     mask_build -> (transpose_v) -> attn_fwd in one call
@@ -212,6 +213,23 @@ int nabla_transpose_v(const nabla_geom* geom, const void* v, void* vt, void* str
 int nabla_attn_fwd_vt(const nabla_geom* geom, const void* q, const void* k,
                       const void* vt, const int32_t* row_ptr, const int32_t* col_idx,
                       float scale, void* o, void* stream);
+
+/* Layout pass after a transformer layer's fused QKV projection, for a
+ * network that keeps its token sequence in the blocked (fractal-flattened)
+ * order throughout ([GZ] Methodology, token reordering and downsampling):
+ * splits the projection output into the head-major tensors the other calls
+ * take and computes the block means on the way, so no pooling or V
+ * transpose pass of its own is needed.  geom: layout NABLA_LAYOUT_BLOCKED
+ * (NABLA_E_LAYOUT otherwise), dtype bf16 (NABLA_E_DTYPE otherwise).
+ *   qkv        bf16 [B, nb * 64, 3, heads, d]: for every token of the blocked
+ *              order (pad slots included) its q, k and v rows of every head
+ *   q, k       out, bf16 [B, heads, nb * 64, d]: copies, blocked layout
+ *   vt         out, bf16 [B, heads, nb, d, 64]: as nabla_transpose_v of v
+ *   qbar, kbar out, float32 [B, heads, nb, d]: bit-identical to nabla_pool
+ *              of q and k (means over the valid tokens; pad slots ignored)
+ * Bit-exact otherwise. */
+int nabla_qkv_split(const nabla_geom* geom, const void* qkv, void* q, void* k,
+                    void* vt, float* qbar, float* kbar, void* stream);
 
 /* Dense (full) attention, the baseline that the method's speed-ups are
  * measured against ([GZ] experimental results 1, speed-up over full

@@ -98,6 +98,11 @@ def test_argument_validation():
                                     None) == -1
     assert lib.nabla_dense_attn_fwd(ctypes.byref(g), FAKE, FAKE, FAKE, 0.0, FAKE, None,
                                     None) == -11
+    assert lib.nabla_qkv_split(ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -9
+    gbl = G(layout=1)
+    assert lib.nabla_qkv_split(ctypes.byref(G(layout=1, dtype=0, out_dtype=0)), FAKE, FAKE, FAKE,
+                               FAKE, FAKE, FAKE, None) == -3
+    assert lib.nabla_qkv_split(ctypes.byref(gbl), FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == -1
     assert lib.nabla_flatten(ctypes.byref(g), None, FAKE, None) == -1
     assert lib.nabla_unflatten(ctypes.byref(g), FAKE, None, None) == -1
     size = ctypes.c_size_t(0)
