@@ -63,6 +63,8 @@ def parse():
                          "with every block kept, torch flash SDPA)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 480p and Long summaries (720p runs only)")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the Wan-shaped attention layer (QKV and output projections on "
                          "hipBLASLt around the NABLA call, tokens in the blocked order)")
@@ -439,8 +441,106 @@ def cpu_baseline(cfg, q, k, v, thr, sta, budget_s, gpu_bits=None, gpu_o=None):
                    f"({t_mask + t_attn:.1f} s CPU); extrapolated to the whole call "
                    f"= {seconds:.0f} s"),
         "seconds_per_call_extrapolated": seconds,
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model(),
+        "os_cpu_count": os.cpu_count(),
+        "cores_note": "cores = BLAS threads the oracle ran with (threadpoolctl)",
     }
+
+
+def popcount_rows(torch, words, nb):
+    """Set bits per row of mask words [..., nb, nw] (bits past nb ignored)."""
+    w = words.cpu().numpy().view(np.uint32)
+    bits = np.unpackbits(w.view(np.uint8), axis=-1, bitorder="little")[..., :nb]
+    return bits.sum(-1, dtype=np.int64)
+
+
+def valid_token_flops(torch, cfg, nb, rp, ci, d):
+    """FLOPs of the kept pairs counted over valid tokens only:
+    4 d * sum over kept (a, b) of valid(a) * valid(b)."""
+    nval = torch.from_numpy(valid_slots(cfg, nb).reshape(nb, 64).sum(1)).to(rp.device)
+    nval = nval.to(torch.float64)
+    total = 0.0
+    for hh in range(rp.shape[0]):
+        nnz_h = int(rp[hh, nb])
+        cs = torch.zeros(nnz_h + 1, dtype=torch.float64, device=rp.device)
+        cs[1:] = torch.cumsum(nval[ci[hh, :nnz_h].long()], 0)
+        row = cs[rp[hh, 1:].long()] - cs[rp[hh, :-1].long()]
+        total += float((row * nval).sum())
+    return 4.0 * d * total
+
+
+def config_summary(torch, nabla, synth, name, time_call, stream):
+    """Stage times, roofline fractions and sparsity of another workload in the
+    same launch configuration (mask construction, V^T, attention)."""
+    cfg = synth.config(name)
+    q, k, v = synth.make_qkv(cfg, device="cuda")
+    g = nabla.Geometry(cfg.batch, cfg.heads, cfg.T, cfg.H, cfg.W, cfg.head_dim, cfg.torch_dtype)
+    B, h, nb, d = cfg.batch, cfg.heads, g.nb, cfg.head_dim
+    dev = q.device
+    qbar = torch.empty((B, h, nb, d), dtype=torch.float32, device=dev)
+    kbar = torch.empty_like(qbar)
+    bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
+    abits = torch.empty_like(bits)
+    cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)
+    rp = torch.empty((B * h, nb + 1), dtype=torch.int32, device=dev)
+    ci = torch.empty((B * h, nb * nb), dtype=torch.int32, device=dev)
+    vt = torch.empty(nabla.vt_shape(g), dtype=q.dtype, device=dev)
+    o = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(d)
+    mc_ms = time_call(lambda: nabla.nabla_mask_build(g, q, k, cfg.thr, cfg.sta, qbar, kbar, bits,
+                                                     cnt, abits, rp, ci, stream), reps=3)
+    vt_ms = time_call(lambda: nabla.nabla_transpose_v(g, v, vt, stream), reps=3)
+    at_ms = time_call(lambda: nabla.nabla_attn_fwd_vt(g, q, k, vt, rp, ci, scale, o, stream),
+                      reps=3)
+    torch.cuda.synchronize()
+    nnz = int(cnt.to(torch.int64).sum())
+    n_ad = int(popcount_rows(torch, abits, nb).sum())
+    flops = nnz * 4 * 64 * 64 * d
+    mc_bytes = sum(algorithmic_bytes(cfg, nb, nnz))
+    out = {"workload": WORKLOAD_NAMES[name], "thr": cfg.thr, "sta": list(cfg.sta),
+           "blocks_per_head": nb,
+           "sparsity": round(1.0 - nnz / (B * h * nb * nb), 4),
+           "sparsity_adaptive_only": round(1.0 - n_ad / (B * h * nb * nb), 4),
+           "mask_construction_ms": round(mc_ms, 4),
+           "mask_construction_frac": round(mc_bytes / (mc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "transpose_v_ms": round(vt_ms, 4),
+           "attn_ms": round(at_ms, 3),
+           "attn_tflops": round(flops / (at_ms * 1e-3) / 1e12, 1),
+           "attn_frac": round(flops / (at_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    del q, k, v, qbar, kbar, bits, abits, cnt, rp, ci, vt, o
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def mask_accuracy(cfg, q, k, thr, sta, heads, gpu_bits):
+    """Band rows and differing rows of the GPU's mask against the oracle's on
+    the given heads (float64 oracle, CPU)."""
+    import oracle as O
+    g = O.Geometry(cfg.T, cfg.H, cfg.W, cfg.P)
+    valid = O.valid_tokens(g)
+    out = []
+    for hh in heads:
+        qb = O.flatten(q[0, hh].double().cpu().numpy(), g)
+        kb = O.flatten(k[0, hh].double().cpu().numpy(), g)
+        m, m_ad, p = O.nabla_mask(O.pool(qb, valid), O.pool(kb, valid), thr, g, sta)
+        band_a, band_b = O.band_rows(p, m_ad, thr)
+        words = gpu_bits[hh].astype(np.uint32)
+        gm = ((words[:, np.arange(g.nb) >> 5] >> (np.arange(g.nb) & 31)) & 1).astype(bool)
+        diff = (gm != m).any(1)
+        out.append({"head": int(hh), "band_rows_a": int(band_a.sum()),
+                    "band_rows_b": int(band_b.sum()), "differing_rows": int(diff.sum()),
+                    "differing_rows_outside_band": int((diff & ~(band_a | band_b)).sum())})
+    return out
 
 
 def main():
@@ -574,6 +674,12 @@ def main():
     kept_flops = nnz * 4 * 64 * 64 * d
     sparsity = 1.0 - nnz / (B * h * nb * nb)
     per_row = counts.flatten().float()
+    abits = torch.empty_like(bits)
+    nabla.nabla_mask(g, qbar, kbar, thr, sta, bits, cnt, abits, stream)
+    torch.cuda.synchronize()
+    n_adaptive = int(popcount_rows(torch, abits, nb).sum())
+    del abits
+    valid_flops = valid_token_flops(torch, cfg, nb, rp, ci, d)
     pool_b, mask_b, compact_b = algorithmic_bytes(cfg, nb, nnz)
     mc_bytes = pool_b + mask_b + compact_b
     mc_ms = stages["mask_build"]
@@ -610,9 +716,13 @@ def main():
             "frac": round(attn_tflops / BF16_PEAK_TFLOPS, 4),
             "traffic": traffic_record(vt_path and cfg.name == "720p" and args.heads is None
                                       and args.thr is None and args.sta is None),
-            "traffic_unit": "bytes per launch (HBM, counter-calibrated)",
+            "traffic_unit": "bytes per launch fetched and written beyond L2 (Infinity Cache "
+                            "and HBM; FETCH_SIZE / WRITE_SIZE, copy-calibrated)",
             "work_per_launch": f"{nnz} kept 64x64 block pairs x 4*64*64*{d} flop = "
-                               f"{kept_flops / 1e12:.3f} TFLOP",
+                               f"{kept_flops / 1e12:.3f} TFLOP (pad slots of edge blocks "
+                               "included: the kernel computes whole blocks)",
+            "valid_token_tflop": round(valid_flops / 1e12, 3),
+            "valid_token_tflops": round(valid_flops / (attn_avg * 1e-3) / 1e12, 2),
             "avg_launch_ms": round(attn_avg, 4),
         },
         "mask_construction": {
@@ -629,6 +739,7 @@ def main():
         "stages_ms": {k_: round(v_, 4) for k_, v_ in stages.items()},
         "attn_ms_min_median": [round(attn_ms[0], 4), round(attn_ms[len(attn_ms) // 2], 4)],
         "sparsity": round(sparsity, 4),
+        "sparsity_adaptive_only": round(1.0 - n_adaptive / (B * h * nb * nb), 4),
         "kept_per_row_min_mean_max": [int(per_row.min()), round(float(per_row.mean()), 1),
                                       int(per_row.max())],
         "gpu": torch.cuda.get_device_name(0),
@@ -731,6 +842,12 @@ def main():
         result["dense_reference"]["torch_sdpa_flash"] = tf
     if not args.no_layer:
         result["dit_layer"] = layer_leg(torch, nabla, cfg, g, q, thr, sta, scale, time_call, dev)
+    if not args.no_configs and cfg.name == "720p" and args.heads is None:
+        result["other_configs"] = {}
+        for name in ("480p", "long"):
+            result["other_configs"][name] = config_summary(torch, nabla, synth, name, time_call,
+                                                           stream)
+            log(f"{name}: {result['other_configs'][name]}")
     if not args.no_cpu_baseline:
         step()                       # the call's own mask and output again (the legs above
         torch.cuda.synchronize()     # reused the buffers)
@@ -740,6 +857,10 @@ def main():
             gpu_bits=bits[0, 0].cpu().numpy(), gpu_o=o[0, 0].double().cpu().numpy())
         log(f"cpu baseline done: {result['cpu_baseline']['value']:.6f} TFLOP/s; "
             f"head 0 vs the oracle: {result['cpu_baseline']['accuracy_vs_gpu']}")
+        heads = sorted(set(synth.sampled_heads(cfg)) - {0})
+        acc = mask_accuracy(cfg, q, k, thr, sta, heads, bits[0].cpu().numpy())
+        result["cpu_baseline"]["mask_vs_oracle_other_sampled_heads"] = acc
+        log(f"mask vs oracle: {acc}")
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
