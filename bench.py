@@ -91,15 +91,29 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
 
 
+PEAKS_SRC = os.path.join(ROOT, "bench_peaks.hip")
+PEAKS_LIB = os.path.join(ROOT, "bench_peaks.so")
+
+
+def build_peaks(verbose: bool = False) -> str:
+    """Compile the benchmark's rate probe (bench_peaks.hip) into its own small
+    library beside this file; the NABLA library does not contain it."""
+    from block_sparse_attention_flatten_amd.build import HIP_FLAGS, _run, hipcc
+    tmp = PEAKS_LIB + ".tmp"
+    _run([hipcc(), *HIP_FLAGS, "-shared", "-o", tmp, PEAKS_SRC], verbose)
+    os.replace(tmp, PEAKS_LIB)
+    return PEAKS_LIB
+
+
 def achievable_peaks(torch, stream, ev):
     """What this GPU sustains right now, for reading the roofline fractions:
-    back-to-back bf16 matrix instructions on every CU (probe/peaks.hip, its own
+    back-to-back bf16 matrix instructions on every CU (bench_peaks.hip, its own
     library) and a plain 2 GiB device copy.  None if the probe library is not
     built."""
     import ctypes
-    path = os.path.join(ROOT, "block_sparse_attention_flatten_amd", "libnabla_probe.so")
+    path = PEAKS_LIB
     if not os.path.exists(path):
-        log("achievable peaks skipped: libnabla_probe.so not built")
+        log("achievable peaks skipped: bench_peaks.so not built")
         return None
     lib = ctypes.CDLL(path)
     lib.nabla_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
@@ -149,7 +163,7 @@ def achievable_peaks(torch, stream, ev):
         "hbm_copy_gbs": round(2 * 4 * n / (copy_ms * 1e-3) / 1e9, 1),
         "torch_copy_gbs": round(2 * 4 * n / (torch_copy_ms * 1e-3) / 1e9, 1),
         "how": "back-to-back v_mfma_f32_32x32x16_bf16 on all CUs; streaming 2 GiB device copy "
-               "(probe/peaks.hip) and torch's copy_, read + write bytes",
+               "(bench_peaks.hip) and torch's copy_, read + write bytes",
     }
 
 

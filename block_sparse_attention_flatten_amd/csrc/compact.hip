@@ -3,8 +3,7 @@
 //
 // Per head: row_ptr = exclusive prefix sum of the row counts, col_idx = kept
 // block indices of each row in ascending order.  Each wavefront compacts
-// kCompactRows rows of one head (compact_rows in mask_items.hpp, shared with
-// the fused build kernel).
+// kCompactRows rows of one head (compact_rows in mask_items.hpp).
 #include "mask_items.hpp"
 
 namespace nabla {

@@ -1,6 +1,7 @@
-// Device-side pieces of mask construction, shared by the standalone kernels
-// (nabla_pool, nabla_mask, nabla_compact) and the fused build kernel
-// (nabla_mask_build), so that both routes produce identical bits:
+// Device-side pieces of mask construction, each the work of one wavefront,
+// used by the pooling, mask and compaction kernels (pool.hip, mask.hip,
+// compact.hip) and, for the summation order of the means, by the layout pass
+// after a QKV projection (qkv_split.hip):
 //   * pool_block  - the mean of one block's valid tokens ("NABLA:
 //     Neighborhood Adaptive Block-Level Attention", gist.science,
 //     Methodology: downsampling);
@@ -10,8 +11,8 @@
 //     integration with STA);
 //   * compact_rows - rows of a mask expanded into the compressed kept lists
 //     (lsdiaocha.cn article on NABLA, sec. 5: compressed sparse storage).
-// Each piece is the work of one wavefront, so the kernels can hand them to
-// wavefronts in different ways and still produce the same bits.
+// Because each piece is one wavefront's work, a kernel may hand the pieces to
+// its wavefronts in any way and still produce the same bits.
 #pragma once
 
 #include <type_traits>

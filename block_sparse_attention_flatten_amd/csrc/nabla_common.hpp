@@ -104,7 +104,7 @@ hipError_t launch_mask(const Geo& g, const float* qbar, const float* kbar, float
                        hipStream_t s);
 hipError_t launch_compact(const Geo& g, const uint32_t* bits, const int32_t* cnt,
                           int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
-// pool + mask + compact fused into a few launches (mask.hip)
+// pool, mask and compact in order on one stream (mask.hip)
 hipError_t launch_mask_build(const Geo& g, bool bf16, const void* q, const void* k, float* qbar,
                              float* kbar, float thr, const int sta[3], uint32_t* bits,
                              int32_t* cnt, uint32_t* abits, int32_t* row_ptr, int32_t* col_idx,

@@ -3,8 +3,8 @@
 // sec. 2 step 1): the delegate of a block is the mean of its valid tokens.
 //
 // HBM-bound streaming read, one wavefront per block (pool_block in
-// mask_items.hpp, shared with the fused build kernel so both give the same
-// bits).  Both the natural and the blocked layout are addressed in 8-token
+// mask_items.hpp; nabla_qkv_split repeats its summation order, so both give
+// the same bits).  Both the natural and the blocked layout are addressed in 8-token
 // patch rows, so the reorder costs no extra pass.
 #include "mask_items.hpp"
 

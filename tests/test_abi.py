@@ -168,9 +168,9 @@ def test_status_strings():
 
 
 def test_probe_library_exports():
-    """The benchmark's rate probe (probe/peaks.hip) is built beside libnabla and
-    exports its three calls; only bench.py loads it."""
-    path = os.path.join(os.path.dirname(_lib.LIB_PATH), "libnabla_probe.so")
+    """The benchmark's rate probe (bench_peaks.hip) is built beside bench.py,
+    outside the library, and exports its three calls; only bench.py loads it."""
+    path = os.path.join(ROOT, "bench_peaks.so")
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT\s+(nabla_probe_\w+)", out))
