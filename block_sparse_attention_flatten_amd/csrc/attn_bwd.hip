@@ -631,40 +631,44 @@ attn_bwd_dkdv_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
 }
 
 // ---------------------------------------------------------------------------
-// float32 kernels: one thread per token, fp32 FMA
+// float32 kernels: two threads per token (lanes 2t, 2t + 1 hold the two
+// channel halves, dot products are completed with one lane exchange), fp32
+// FMA, tiles in LDS
 // ---------------------------------------------------------------------------
-// dQ and D: one workgroup (64 threads) per query block, K and V tiles in LDS.
+// dQ and D: one workgroup (128 threads) per query block, K and V tiles in LDS.
 template <int D>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(128)
 attn_bwd_dq_f32_kernel(const Geo g, const float* __restrict__ Q, const float* __restrict__ K,
                        const float* __restrict__ V, const float* __restrict__ O,
                        const float* __restrict__ dO, const float* __restrict__ lse,
                        const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
                        float scale, float* __restrict__ dQ, float* __restrict__ delta) {
+  constexpr int H = D / 2;                 // channels per thread
   extern __shared__ __attribute__((aligned(16))) float smem_f[];
   float* Kt = smem_f;
   float* Vt = smem_f + kN * D;
   const int nb = g.nb;
   const int64_t head = blockIdx.x / nb;
   const int qb = (int)(blockIdx.x - head * nb);
-  const int s = threadIdx.x;
+  const int s = threadIdx.x >> 1, c0 = (threadIdx.x & 1) * H;
   const int64_t hoff = head * (int64_t)g.head_elems;
   const int row_step = block_row_step(g);
   const BlockCoord qc = block_coord(g, qb);
   const bool qvalid = (s >> 3) < block_rows_valid(g, qc) && (s & 7) < block_cols_valid(g, qc);
-  const int64_t qoff = hoff + block_base(g, qb, qc) + (s >> 3) * row_step + (s & 7) * D;
+  const int64_t qoff = hoff + block_base(g, qb, qc) + (s >> 3) * row_step + (s & 7) * D + c0;
 
-  float qv[D], dov[D], acc[D];
+  float qv[H], dov[H], acc[H];
   float Dq = 0.f;
 #pragma unroll
-  for (int c = 0; c < D; ++c) {
+  for (int c = 0; c < H; ++c) {
     qv[c] = qvalid ? Q[qoff + c] : 0.f;
     dov[c] = qvalid ? dO[qoff + c] : 0.f;
     Dq = fmaf(dov[c], qvalid ? O[qoff + c] : 0.f, Dq);
     acc[c] = 0.f;
   }
+  Dq += __shfl_xor(Dq, 1);
   const int64_t slot = (head * nb + qb) * kN + s;
-  delta[slot] = Dq;
+  if ((threadIdx.x & 1) == 0) delta[slot] = Dq;
   const float l = lse[slot];
   const bool live = qvalid && l > -INFINITY;
   const int32_t* rp = row_ptr + head * (nb + 1);
@@ -679,7 +683,7 @@ attn_bwd_dq_f32_kernel(const Geo g, const float* __restrict__ Q, const float* __
     const int rv = block_rows_valid(g, bc), cv = block_cols_valid(g, bc);
     const int64_t base = hoff + block_base(g, beta, bc);
     __syncthreads();
-    for (int i = threadIdx.x; i < kN * D / 4; i += 64) {
+    for (int i = threadIdx.x; i < kN * D / 4; i += 128) {
       const int r = i / (D / 4), c4 = i % (D / 4);
       f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
       if ((r >> 3) < rv && (r & 7) < cv) {
@@ -691,35 +695,38 @@ attn_bwd_dq_f32_kernel(const Geo g, const float* __restrict__ Q, const float* __
       *(f32x4*)(Vt + r * D + 4 * c4) = vv;
     }
     __syncthreads();
-    if (!live) continue;
-    for (int r = 0; r < kN; ++r) {
+    for (int r = 0; r < kN; ++r) {     // both lanes of a pair take the same branches
       if (!((r >> 3) < rv && (r & 7) < cv)) continue;
       float dot = 0.f, dp = 0.f;
 #pragma unroll
-      for (int c = 0; c < D; ++c) {
-        dot = fmaf(qv[c], Kt[r * D + c], dot);
-        dp = fmaf(dov[c], Vt[r * D + c], dp);
+      for (int c = 0; c < H; ++c) {
+        dot = fmaf(qv[c], Kt[r * D + c0 + c], dot);
+        dp = fmaf(dov[c], Vt[r * D + c0 + c], dp);
       }
-      const float ds = expf(dot * scale - l) * (dp - Dq);
+      dot += __shfl_xor(dot, 1);
+      dp += __shfl_xor(dp, 1);
+      const float ds = live ? expf(dot * scale - l) * (dp - Dq) : 0.f;
 #pragma unroll
-      for (int c = 0; c < D; ++c) acc[c] = fmaf(ds, Kt[r * D + c], acc[c]);
+      for (int c = 0; c < H; ++c) acc[c] = fmaf(ds, Kt[r * D + c0 + c], acc[c]);
     }
   }
   if (qvalid || g.layout == 1) {
 #pragma unroll
-    for (int c = 0; c < D; ++c) dQ[qoff + c] = qvalid ? acc[c] * scale : 0.f;
+    for (int c = 0; c < H; ++c) dQ[qoff + c] = qvalid ? acc[c] * scale : 0.f;
   }
 }
 
-// dK (threads 64-127) and dV (threads 0-63): one workgroup per key block,
-// the Q and dO tiles of each listed query block in LDS.
+// dK (threads 128-255) and dV (threads 0-127), two threads per key: one
+// workgroup per key block, the Q and dO tiles of each listed query block in
+// LDS.
 template <int D>
-__global__ void __launch_bounds__(128)
+__global__ void __launch_bounds__(256)
 attn_bwd_dkdv_f32_kernel(const Geo g, const float* __restrict__ Q, const float* __restrict__ K,
                          const float* __restrict__ V, const float* __restrict__ dO,
                          const float* __restrict__ lse, const float* __restrict__ delta,
                          const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx,
                          float scale, float* __restrict__ dK, float* __restrict__ dV) {
+  constexpr int H = D / 2;
   extern __shared__ __attribute__((aligned(16))) float smem_f[];
   float* Qt = smem_f;
   float* Gt = smem_f + kN * D;        // dO tile
@@ -728,17 +735,17 @@ attn_bwd_dkdv_f32_kernel(const Geo g, const float* __restrict__ Q, const float* 
   const int nb = g.nb;
   const int64_t head = blockIdx.x / nb;
   const int kb = (int)(blockIdx.x - head * nb);
-  const int s = threadIdx.x & 63;
-  const bool dk_side = threadIdx.x >= 64;
+  const int s = (threadIdx.x & 127) >> 1, c0 = (threadIdx.x & 1) * H;
+  const bool dk_side = threadIdx.x >= 128;   // wavefront-uniform
   const int64_t hoff = head * (int64_t)g.head_elems;
   const int row_step = block_row_step(g);
   const BlockCoord kc = block_coord(g, kb);
   const bool kvalid = (s >> 3) < block_rows_valid(g, kc) && (s & 7) < block_cols_valid(g, kc);
-  const int64_t koff = hoff + block_base(g, kb, kc) + (s >> 3) * row_step + (s & 7) * D;
+  const int64_t koff = hoff + block_base(g, kb, kc) + (s >> 3) * row_step + (s & 7) * D + c0;
 
-  float kv[D], vv[D], acc[D];
+  float kv[H], vv[H], acc[H];
 #pragma unroll
-  for (int c = 0; c < D; ++c) {
+  for (int c = 0; c < H; ++c) {
     kv[c] = kvalid ? K[koff + c] : 0.f;
     vv[c] = kvalid && dk_side ? V[koff + c] : 0.f;
     acc[c] = 0.f;
@@ -755,7 +762,7 @@ attn_bwd_dkdv_f32_kernel(const Geo g, const float* __restrict__ Q, const float* 
     const int rv = block_rows_valid(g, ac), cv = block_cols_valid(g, ac);
     const int64_t base = hoff + block_base(g, alpha, ac);
     __syncthreads();
-    for (int i = threadIdx.x; i < kN * D / 4; i += 128) {
+    for (int i = threadIdx.x; i < kN * D / 4; i += 256) {
       const int r = i / (D / 4), c4 = i % (D / 4);
       f32x4 qq = {0.f, 0.f, 0.f, 0.f}, gg = {0.f, 0.f, 0.f, 0.f};
       if ((r >> 3) < rv && (r & 7) < cv) {
@@ -771,23 +778,24 @@ attn_bwd_dkdv_f32_kernel(const Geo g, const float* __restrict__ Q, const float* 
       Dt[threadIdx.x] = delta[(head * nb + alpha) * kN + threadIdx.x];
     }
     __syncthreads();
-    if (!kvalid) continue;
-    for (int r = 0; r < kN; ++r) {
+    for (int r = 0; r < kN; ++r) {     // both lanes of a pair take the same branches
       if (!((r >> 3) < rv && (r & 7) < cv) || !(Lt[r] > -INFINITY)) continue;
       float dot = 0.f;
 #pragma unroll
-      for (int c = 0; c < D; ++c) dot = fmaf(Qt[r * D + c], kv[c], dot);
-      const float p = expf(dot * scale - Lt[r]);
+      for (int c = 0; c < H; ++c) dot = fmaf(Qt[r * D + c0 + c], kv[c], dot);
+      dot += __shfl_xor(dot, 1);
+      const float p = kvalid ? expf(dot * scale - Lt[r]) : 0.f;
       if (dk_side) {
         float dp = 0.f;
 #pragma unroll
-        for (int c = 0; c < D; ++c) dp = fmaf(Gt[r * D + c], vv[c], dp);
+        for (int c = 0; c < H; ++c) dp = fmaf(Gt[r * D + c0 + c], vv[c], dp);
+        dp += __shfl_xor(dp, 1);
         const float ds = p * (dp - Dt[r]);
 #pragma unroll
-        for (int c = 0; c < D; ++c) acc[c] = fmaf(ds, Qt[r * D + c], acc[c]);
+        for (int c = 0; c < H; ++c) acc[c] = fmaf(ds, Qt[r * D + c0 + c], acc[c]);
       } else {
 #pragma unroll
-        for (int c = 0; c < D; ++c) acc[c] = fmaf(p, Gt[r * D + c], acc[c]);
+        for (int c = 0; c < H; ++c) acc[c] = fmaf(p, Gt[r * D + c0 + c], acc[c]);
       }
     }
   }
@@ -795,7 +803,7 @@ attn_bwd_dkdv_f32_kernel(const Geo g, const float* __restrict__ Q, const float* 
     float* dst = (dk_side ? dK : dV) + koff;
     const float mul = kvalid ? (dk_side ? scale : 1.0f) : 0.f;
 #pragma unroll
-    for (int c = 0; c < D; ++c) dst[c] = acc[c] * mul;
+    for (int c = 0; c < H; ++c) dst[c] = acc[c] * mul;
   }
 }
 
@@ -822,7 +830,7 @@ hipError_t launch_dq_t(const Geo& g, bool bf16, const void* q, const void* k, co
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(g.bh * g.nb)), dim3(64), lds, s, g, (const float*)q,
+  hipLaunchKernelGGL(kern, dim3((unsigned)(g.bh * g.nb)), dim3(128), lds, s, g, (const float*)q,
                      (const float*)k, (const float*)v, (const float*)o, (const float*)dout, lse,
                      row_ptr, col_idx, scale, (float*)dq, delta);
   return hipGetLastError();
@@ -851,7 +859,7 @@ hipError_t launch_dkdv_t(const Geo& g, bool bf16, const void* q, const void* k, 
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(g.bh * g.nb)), dim3(128), lds, s, g, (const float*)q,
+  hipLaunchKernelGGL(kern, dim3((unsigned)(g.bh * g.nb)), dim3(256), lds, s, g, (const float*)q,
                      (const float*)k, (const float*)v, (const float*)dout, lse, delta, col_ptr,
                      row_idx, scale, (float*)dk, (float*)dv);
   return hipGetLastError();

@@ -27,8 +27,8 @@
 // Pad keys (latent edge blocks) get -inf scores; pad queries are not written
 // (blocked layout: written as zeros).
 //
-// fp32 path: a plain kernel (one thread per query, fp32 FMA, K/V tiles in
-// LDS) used for float32 inputs.
+// fp32 path: one query block per workgroup on fp32 matrix cores, K/V tiles
+// in LDS (below), used for float32 inputs.
 #include "attn_common.hpp"
 
 namespace nabla {
@@ -283,33 +283,59 @@ attn_fwd_bf16_kernel(const Geo g, const __bf16* __restrict__ Q, const __bf16* __
 }
 
 // ---------------------------------------------------------------------------
-// float32 path: one thread per query token, fp32 FMA, exact online softmax
+// float32 path on fp32 matrix cores (v_mfma_f32_16x16x4f32).  One workgroup of
+// four wavefronts per query block walks its kept list; wavefront w owns
+// queries 16w .. 16w + 15.  The K and V tiles (64 x d float32) are staged in
+// LDS with rows padded by 16 bytes, so the 16 rows a read instruction touches
+// fall on distinct banks.
+//   * S^T = K Q^T: lane l supplies key row 16 kt + l % 16 and query l % 16;
+//     the contraction index is permuted the same way for both operands
+//     (step s, lane group r = l / 16 supplies element r d/4 + s), so each
+//     lane's operands are contiguous.  The result gives lane l the scores of
+//     query l % 16 against keys 16 kt + 4 (l / 16) + i, i < 4.
+//   * O^T += V^T P^T: with keys ordered the same way inside each 4-key step,
+//     the B operand is the lane's own score slot and the A operand one float
+//     of the V tile, so P never leaves the registers.
+//   * Online softmax in the exp2 domain in float32 (no rounding of P); the
+//     row max is taken over the four lanes that share a query.
+// Pad keys get -inf scores; pad queries are not written (blocked layout:
+// zeros).
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(256)
 attn_fwd_f32_kernel(const Geo g, const float* __restrict__ Q, const float* __restrict__ K,
                     const float* __restrict__ V, const int32_t* __restrict__ row_ptr,
-                    const int32_t* __restrict__ col_idx, float scale, float* __restrict__ O,
+                    const int32_t* __restrict__ col_idx, float scale_log2, float* __restrict__ O,
                     float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) float Kt[kN * D];
-  __shared__ __attribute__((aligned(16))) float Vt[kN * D];
+  constexpr int kStride = D + 4;           // LDS row stride (floats)
+  constexpr int kQ = D / 4;                // contraction steps per 16 x 16 score tile
+  constexpr int kDT = D / 16;              // 16-channel tiles of O^T
+  __shared__ __attribute__((aligned(16))) float Kt[kN * kStride];
+  __shared__ __attribute__((aligned(16))) float Vt[kN * kStride];
   const int nb = g.nb;
   const int64_t head = blockIdx.x / nb;
   const int qb = (int)(blockIdx.x - head * nb);
-  const int s = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, r = lane >> 4;
   const int64_t hoff = head * (int64_t)g.head_elems;
   const int row_step = block_row_step(g);
   const BlockCoord qc = block_coord(g, qb);
-  const bool qvalid = (s >> 3) < block_rows_valid(g, qc) && (s & 7) < block_cols_valid(g, qc);
-  const int64_t qoff = hoff + block_base(g, qb, qc) + (s >> 3) * row_step + (s & 7) * D;
+  const int qs = 16 * wave + n;            // this lane's query slot in the block
+  const bool qvalid = (qs >> 3) < block_rows_valid(g, qc) && (qs & 7) < block_cols_valid(g, qc);
+  const int64_t qoff = hoff + block_base(g, qb, qc) + (qs >> 3) * row_step + (qs & 7) * D;
 
-  float qv[D], acc[D];
+  float qop[kQ];                           // Q[qs][r d/4 + s]
 #pragma unroll
-  for (int c = 0; c < D; ++c) {
-    qv[c] = qvalid ? Q[qoff + c] : 0.f;
-    acc[c] = 0.f;
+  for (int c = 0; c < kQ; c += 4) {
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (qvalid) x = *(const f32x4*)(Q + qoff + r * kQ + c);
+    qop[c] = x[0]; qop[c + 1] = x[1]; qop[c + 2] = x[2]; qop[c + 3] = x[3];
   }
-  float m = -INFINITY, l = 0.f;
+  f32x4 oacc[kDT];                         // O[qs][16 dt + 4 r + i]
+#pragma unroll
+  for (int t = 0; t < kDT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;    // exp2 domain; l_run: this lane's keys only
+
   const int32_t* rp = row_ptr + head * (nb + 1);
   const int32_t* cols = col_idx + head * (int64_t)nb * nb;
   const int begin = rp[qb];
@@ -322,39 +348,74 @@ attn_fwd_f32_kernel(const Geo g, const float* __restrict__ Q, const float* __res
     const int rv = block_rows_valid(g, bc), cv = block_cols_valid(g, bc);
     const int64_t base = hoff + block_base(g, beta, bc);
     __syncthreads();
-    for (int i = threadIdx.x; i < kN * D / 4; i += 64) {
-      const int r = i / (D / 4), c4 = i % (D / 4);
+    for (int i = threadIdx.x; i < kN * D / 4; i += 256) {
+      const int row = i / (D / 4), c4 = i % (D / 4);
       f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-      if ((r >> 3) < rv && (r & 7) < cv) {
-        const int64_t off = base + (r >> 3) * row_step + (r & 7) * D + 4 * c4;
+      if ((row >> 3) < rv && (row & 7) < cv) {
+        const int64_t off = base + (row >> 3) * row_step + (row & 7) * D + 4 * c4;
         kv = *(const f32x4*)(K + off);
         vv = *(const f32x4*)(V + off);
       }
-      *(f32x4*)(Kt + r * D + 4 * c4) = kv;
-      *(f32x4*)(Vt + r * D + 4 * c4) = vv;
+      *(f32x4*)(Kt + row * kStride + 4 * c4) = kv;
+      *(f32x4*)(Vt + row * kStride + 4 * c4) = vv;
     }
     __syncthreads();
-    for (int r = 0; r < kN; ++r) {
-      if (!((r >> 3) < rv && (r & 7) < cv)) continue;
-      float dot = 0.f;
+    // scores of this lane's query against keys 16 kt + 4 r + i
+    f32x4 sc[4];
 #pragma unroll
-      for (int c = 0; c < D; ++c) dot = fmaf(qv[c], Kt[r * D + c], dot);
-      const float x = dot * scale;
-      const float m_new = fmaxf(m, x);
-      const float corr = expf(m - m_new);
-      const float p = expf(x - m_new);
-      l = l * corr + p;
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const float* krow = Kt + (16 * kt + n) * kStride + r * kQ;
 #pragma unroll
-      for (int c = 0; c < D; ++c) acc[c] = fmaf(p, Vt[r * D + c], acc[c] * corr);
-      m = m_new;
+      for (int c = 0; c < kQ; c += 4) {
+        const f32x4 a = *(const f32x4*)(krow + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], qop[c + j], acc, 0, 0, 0);
+      }
+      sc[kt] = acc;
     }
-  }
-  if (lse != nullptr)
-    lse[(head * nb + qb) * kN + s] = qvalid && l > 0.f ? m + logf(l) : -INFINITY;
-  if (qvalid || g.layout == 1) {
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    float mx = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < D; ++c) O[qoff + c] = qvalid ? acc[c] * inv : 0.f;
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * kt + 4 * r + i;
+        const bool ok = (key >> 3) < rv && (key & 7) < cv;
+        sc[kt][i] = ok ? sc[kt][i] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sc[kt][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);  // finite: every kept block has a valid key
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first block
+    m_run = m_new;
+    l_run *= corr;
+#pragma unroll
+    for (int t = 0; t < kDT; ++t) oacc[t] *= corr;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(sc[kt][i] - m_new);   // pad keys: 0
+        l_run += p;
+        const float* vrow = Vt + (16 * kt + 4 * r + i) * kStride + n;
+#pragma unroll
+        for (int t = 0; t < kDT; ++t)
+          oacc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[16 * t], p, oacc[t], 0, 0, 0);
+      }
+  }
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (lse != nullptr && r == 0)            // ln sum exp(s * scale) = (m + log2 l) ln 2
+    lse[(head * nb + qb) * kN + qs] =
+        qvalid && l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+  if (qvalid || g.layout == 1) {
+    // oacc[t][i] = O^T[16 t + 4 r + i][n]; a store per lane group of 4 channels
+    const float inv = qvalid && l_tot > 0.f ? 1.0f / l_tot : 0.f;
+#pragma unroll
+    for (int t = 0; t < kDT; ++t)
+      *(f32x4*)(O + qoff + 16 * t + 4 * r) = oacc[t] * inv;
   }
 }
 
@@ -385,9 +446,9 @@ template <int D>
 void launch_f32(const Geo& g, const void* q, const void* k, const void* v,
                 const int32_t* row_ptr, const int32_t* col_idx, float scale, void* o,
                 float* lse, hipStream_t s) {
-  hipLaunchKernelGGL(attn_fwd_f32_kernel<D>, dim3((unsigned)(g.bh * g.nb)), dim3(64), 0, s, g,
-                     (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx, scale,
-                     (float*)o, lse);
+  hipLaunchKernelGGL(attn_fwd_f32_kernel<D>, dim3((unsigned)(g.bh * g.nb)), dim3(256), 0, s, g,
+                     (const float*)q, (const float*)k, (const float*)v, row_ptr, col_idx,
+                     scale * 1.4426950408889634f, (float*)o, lse);
 }
 
 }  // namespace

@@ -140,3 +140,76 @@ def test_forward_and_backward_graph_replays_match_eager():
                     if a.dtype == torch.bfloat16 else torch.equal(a, b))
             assert same, f"replay {rep}: {name} differs from the eager call"
         log(f"replay {rep}: o, lse, dq, dk, dv, delta match the eager call")
+
+
+def test_noalloc_and_layer_calls_graph_replays_match_eager():
+    """nabla_forward_noalloc (library scratch array), and the layer path
+    (nabla_qkv_split, mask, lists, attention) with the dense kernel, captured
+    in one graph and replayed on new inputs: every replay equals the eager
+    calls bit for bit."""
+    cfg = synth.config("480p", heads=3, T=3)
+    log(f"graph test (no-alloc + layer path) {cfg}")
+    g = nabla.Geometry(cfg.batch, cfg.heads, cfg.T, cfg.H, cfg.W, cfg.head_dim, torch.bfloat16)
+    gb = g.with_layout(nabla.LAYOUT_BLOCKED)
+    B, h, nb, d = cfg.batch, cfg.heads, g.nb, cfg.head_dim
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = (torch.zeros(g.tensor_shape(), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    qkv = torch.zeros(nabla.qkv_shape(gb), dtype=torch.bfloat16, device="cuda")
+
+    def fill(seed):
+        c = cfg.with_(seed=seed)
+        qq, kk, vv = synth.make_qkv(c, device="cuda")
+        q.copy_(qq)
+        k.copy_(kk)
+        v.copy_(vv)
+        # the same fields as a token-major projection output in the blocked order
+        for i, x in enumerate((qq, kk, vv)):
+            xb = torch.empty(gb.tensor_shape(), dtype=torch.bfloat16, device="cuda")
+            nabla.nabla_flatten(g, x, xb)
+            qkv[:, :, i] = xb.permute(0, 2, 3, 1, 4).reshape(B, nb * 64, h, d)
+
+    def step():
+        dev = q.device
+        o1 = torch.empty_like(q)
+        nabla.nabla_forward_noalloc(g, q, k, v, cfg.thr, cfg.sta, scale, o1)
+        qb = torch.empty(gb.tensor_shape(), dtype=torch.bfloat16, device=dev)
+        kb = torch.empty_like(qb)
+        vt = torch.empty(nabla.vt_shape(gb), dtype=torch.bfloat16, device=dev)
+        qbar = torch.empty((B, h, nb, d), dtype=torch.float32, device=dev)
+        kbar = torch.empty_like(qbar)
+        bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)
+        rp = torch.empty((B * h, nb + 1), dtype=torch.int32, device=dev)
+        ci = torch.empty((B * h, nb * nb), dtype=torch.int32, device=dev)
+        o2 = torch.empty_like(qb)
+        o3 = torch.empty_like(qb)
+        nabla.nabla_qkv_split(gb, qkv, qb, kb, vt, qbar, kbar)
+        nabla.nabla_mask(gb, qbar, kbar, cfg.thr, cfg.sta, bits, cnt, None)
+        nabla.nabla_compact(gb, bits, cnt, rp, ci)
+        nabla.nabla_attn_fwd_vt(gb, qb, kb, vt, rp, ci, scale, o2)
+        nabla.nabla_dense_attn_fwd(gb, qb, kb, vt, scale, o3, None)
+        return {"noalloc": o1, "layer": o2, "dense": o3, "qbar": qbar, "bits": bits}
+
+    fill(cfg.seed)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = step()
+    torch.cuda.synchronize()
+    for rep, seed in enumerate([301, 302, 303]):
+        fill(seed)
+        ref = step()                                           # eager reference
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a in out.items():
+            b = ref[name]
+            same = (torch.equal(a.view(torch.int16), b.view(torch.int16))
+                    if a.dtype == torch.bfloat16 else torch.equal(a, b))
+            assert same, f"replay {rep}: {name} differs from the eager call"
+        log(f"replay {rep}: no-alloc, layer-path and dense outputs match the eager calls")
