@@ -232,8 +232,8 @@ def layer_leg(torch, nabla, cfg, g, x_field, thr, sta, scale, time_call, dev):
     Wqkv = (torch.randn(D, 3 * D, generator=gen, device=dev) / math.sqrt(D)).to(torch.bfloat16)
     Wo = (torch.randn(D, D, generator=gen, device=dev) / math.sqrt(D)).to(torch.bfloat16)
     gb = g.with_layout(nabla.LAYOUT_BLOCKED)
-    qbar = torch.empty((1, h, nb, d), dtype=torch.float32, device=dev)
-    kbar = torch.empty_like(qbar)
+    qbar = torch.empty(nabla.qbar_shape(gb), dtype=torch.float32, device=dev)
+    kbar = torch.empty(nabla.kbar_shape(gb), dtype=torch.float32, device=dev)
     bits = torch.empty((1, h, nb, g.nw), dtype=torch.int32, device=dev)
     cnt = torch.empty((1, h, nb), dtype=torch.int32, device=dev)
     rp = torch.empty((h, nb + 1), dtype=torch.int32, device=dev)
@@ -491,8 +491,8 @@ def config_summary(torch, nabla, synth, name, time_call, stream):
     g = nabla.Geometry(cfg.batch, cfg.heads, cfg.T, cfg.H, cfg.W, cfg.head_dim, cfg.torch_dtype)
     B, h, nb, d = cfg.batch, cfg.heads, g.nb, cfg.head_dim
     dev = q.device
-    qbar = torch.empty((B, h, nb, d), dtype=torch.float32, device=dev)
-    kbar = torch.empty_like(qbar)
+    qbar = torch.empty(nabla.qbar_shape(g), dtype=torch.float32, device=dev)
+    kbar = torch.empty(nabla.kbar_shape(g), dtype=torch.float32, device=dev)
     bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
     abits = torch.empty_like(bits)
     cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)
@@ -584,8 +584,8 @@ def main():
     g = nabla.Geometry(cfg.batch, cfg.heads, cfg.T, cfg.H, cfg.W, cfg.head_dim, cfg.torch_dtype)
     B, h, nb, d = cfg.batch, cfg.heads, g.nb, cfg.head_dim
     dev = q.device
-    qbar = torch.empty((B, h, nb, d), dtype=torch.float32, device=dev)
-    kbar = torch.empty_like(qbar)
+    qbar = torch.empty(nabla.qbar_shape(g), dtype=torch.float32, device=dev)
+    kbar = torch.empty(nabla.kbar_shape(g), dtype=torch.float32, device=dev)
     bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)
     rp = torch.empty((B * h, nb + 1), dtype=torch.int32, device=dev)

@@ -87,7 +87,7 @@ void workspace_parts(const Geo& g, bool bf16, size_t off[kWsParts], size_t* tota
   const size_t bh = (size_t)g.bh, nb = (size_t)g.nb, nw = (nb + 31) / 32;
   const size_t sizes[kWsParts] = {
       bh * nb * g.d * sizeof(float),        // qbar
-      bh * nb * g.d * sizeof(float),        // kbar
+      bh * (size_t)nabla::kbar_rows(g.nb) * g.d * sizeof(float),   // kbar (tiled)
       bh * nb * nw * sizeof(uint32_t),      // mask bits
       bh * nb * sizeof(int32_t),            // row counts
       bh * (nb + 1) * sizeof(int32_t),      // row_ptr

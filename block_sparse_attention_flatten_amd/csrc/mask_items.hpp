@@ -159,6 +159,21 @@ __device__ inline void pool_block(const Geo& g, const T* x, int b,
   for (int e = 0; e < S::kElems; ++e) mean[e] *= inv;
 }
 
+// Store pool_block's result as row `row` of a head's pooled keys in the
+// tiled order (kbar_offset): four consecutive channels stay contiguous.
+template <typename T, int D>
+__device__ inline void store_mean_tiled(const float (&mean)[PoolShape<T, D>::kElems],
+                                        float* head_base, int row) {
+  using S = PoolShape<T, D>;
+  const int lane = threadIdx.x & 63;
+  if (lane < S::kLanesPerRow) {
+#pragma unroll
+    for (int e = 0; e < S::kElems; e += 4)
+      *(f32x4*)(head_base + kbar_offset(row, lane * S::kElems + e, D)) =
+          f32x4{mean[e], mean[e + 1], mean[e + 2], mean[e + 3]};
+  }
+}
+
 // Store pool_block's result to dst[0 .. D) (global or LDS).
 template <typename T, int D>
 __device__ inline void store_mean(const float (&mean)[PoolShape<T, D>::kElems], float* dst) {
@@ -451,7 +466,7 @@ __device__ inline void score_tiles(const Geo& g, const MaskArgs& a, int64_t head
                                    float* S, int first, int step, int rot) {
   const int nb = g.nb;
   const int lane = threadIdx.x & 63;
-  const float* Kh = a.kbar + head * nb * D;
+  const float* Kh = a.kbar + head * kbar_rows(nb) * D;   // tiled (kbar_offset)
   const float* Qh = a.qbar + head * nb * D;
   const int i16 = lane & 15;          // A row / B column of this lane
   const int g4 = lane >> 4;           // k sub-index
@@ -469,11 +484,12 @@ __device__ inline void score_tiles(const Geo& g, const MaskArgs& a, int64_t head
     aop[t] = arow ? *(const f32x4*)(Qh + (int64_t)qrow * D + 16 * t + 4 * g4)
                   : f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K rows through a buffer descriptor over the head's K: the lane's part of
-  // the offset is fixed, the tile's part scalar; lanes past the last block
-  // get an offset beyond the descriptor and load zeros.
-  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kh, (uint32_t)(nb * D * 4));
-  const uint32_t lane_off = (uint32_t)((i16 * D + 4 * g4) * 4);
+  // K rows through a buffer descriptor over the head's pooled keys.  In
+  // their tiled order, load t of a tile gives lane l the 16 bytes at
+  // (64 t + l) * 16: row i16, channels 16t + 4 g4 .. + 3, one contiguous
+  // kilobyte per load.  Lanes of rows past the last block load zeros.
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kh, (uint32_t)(kbar_rows(nb) * D * 4));
+  const uint32_t lane_off = (uint32_t)(lane * 16);
   auto load_b = [&](int ct, f32x4 (&bv)[D / 16]) {
     const uint32_t voff = ct * 16 + i16 < nb ? lane_off : 0x80000000u;
     // the tile offset is wavefront-uniform; say so, or the compiler wraps
@@ -482,7 +498,7 @@ __device__ inline void score_tiles(const Geo& g, const MaskArgs& a, int64_t head
 #pragma unroll
     for (int t = 0; t < D / 16; ++t)
       bv[t] = __builtin_bit_cast(
-          f32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff + 64u * t, soff, 0));
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff + 1024u * t, soff, 0));
   };
   // two accumulators (even and odd k-chunks) so consecutive matrix
   // instructions do not wait on each other; one fixed summation order

@@ -49,6 +49,14 @@ struct Geo {
   Recip gw_r;        // division by gw
 };
 
+// Pooled keys are stored in tiles of 16 blocks, in the order the mask
+// kernel's matrix-core operand loads read them: float offset of (block row,
+// channel c) within a head, and the padded row count of a head.
+__host__ __device__ inline int kbar_rows(int nb) { return (nb + 15) & ~15; }
+__host__ __device__ inline int kbar_offset(int row, int c, int d) {
+  return (row >> 4) * 16 * d + (((c >> 4) << 2) + ((c >> 2) & 3)) * 64 + (row & 15) * 4 + (c & 3);
+}
+
 struct BlockCoord {
   int t, hb, wb;
 };

@@ -24,10 +24,12 @@ __global__ void __launch_bounds__(256) pool_kernel(const Geo g, const T* __restr
   const int64_t head = gb / g.nb;
   const int b = (int)(gb - head * g.nb);
   const T* x = (blockIdx.y == 0 ? q : k) + head * (int64_t)g.head_elems;
-  float* out = (blockIdx.y == 0 ? qbar : kbar) + gb * D;
   float mean[PoolShape<T, D>::kElems];
   mask_detail::pool_block<T, D>(g, x, b, mean);
-  mask_detail::store_mean<T, D>(mean, out);
+  if (blockIdx.y == 0)
+    mask_detail::store_mean<T, D>(mean, qbar + gb * D);
+  else
+    mask_detail::store_mean_tiled<T, D>(mean, kbar + head * kbar_rows(g.nb) * D, b);
 }
 
 template <typename T, int D>

@@ -7,7 +7,8 @@
 // This pass reads each (block, head) tile once and writes
 //   q, k   head-major copies in the blocked layout,
 //   V^T    the attention kernel's transposed V operand (as nabla_transpose_v),
-//   q̄, k̄   the means of the block's valid tokens (as nabla_pool, same bits),
+//   q̄, k̄   the means of the block's valid tokens (as nabla_pool, same bits
+//          and the same tiled order for k̄),
 // so pooling and the V transpose cost no pass of their own.
 //
 // One workgroup per (block, head, batch): the 3 x 64 token rows are read with
@@ -83,7 +84,10 @@ __global__ void __launch_bounds__(256) qkv_split_kernel(const Geo g, int heads,
     const float inv = 1.0f / (float)(rv * cv);
 #pragma unroll
     for (int e = 0; e < S::kElems; ++e) mean[e] *= inv;
-    mask_detail::store_mean<__bf16, D>(mean, (wave == 0 ? qbar : kbar) + (head * g.nb + b) * D);
+    if (wave == 0)
+      mask_detail::store_mean<__bf16, D>(mean, qbar + (head * g.nb + b) * D);
+    else
+      mask_detail::store_mean_tiled<__bf16, D>(mean, kbar + head * kbar_rows(g.nb) * D, b);
   }
 
   // V^T: row = channel, keys permuted inside each group of 16 by swapping

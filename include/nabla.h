@@ -62,7 +62,13 @@
  *                         pad slots present in memory and ignored on input)
  *   Q, K, V and O of one call share one layout, contiguous; Q, K, V share
  *   `dtype` and O has `out_dtype`.
- *   Pooled tensors qbar, kbar: float32 [B, heads, nb, d].
+ *   Pooled queries qbar: float32 [B, heads, nb, d] (row c = block c).
+ *   Pooled keys kbar: float32 [B, heads, nb16, d], nb16 = 16 * ceil(nb / 16),
+ *        in the mask kernel's matrix-core operand order: blocks in tiles of
+ *        16 rows, and inside tile j the value of block 16 j + i, channel c at
+ *        float offset 16 j d + ((c / 16) * 4 + (c / 4) % 4) * 64 + 4 i + c % 4,
+ *        so that one 16-byte-per-lane load of a wavefront is 1 KB contiguous.
+ *        Rows past nb are ignored on input and left unwritten on output.
  *   Masks: uint32 [B, heads, nb, nw], nw = ceil(nb / 32); block c of row r is
  *   kept iff bit (c % 32) of word (c / 32) is set.  Bits >= nb are zero.
  *   Row counts: int32 [B, heads, nb].
@@ -84,7 +90,7 @@
 extern "C" {
 #endif
 
-#define NABLA_ABI_VERSION 3
+#define NABLA_ABI_VERSION 4
 
 enum nabla_status {
   NABLA_OK = 0,
@@ -138,8 +144,8 @@ int nabla_unflatten(const nabla_geom* geom, const void* x_blocked, void* x, void
 
 /* Block average pooling of Q and K ([GZ] Methodology, downsampling;
  * [LS] sec. 2 and 4): qbar[b, h, c, :] = mean of the valid tokens of block c,
- * accumulated in float32.  q, k in geom's layout and dtype; qbar, kbar
- * float32 [B, heads, nb, d]. */
+ * accumulated in float32, and the same for kbar in its tiled order (see the
+ * layouts above).  q, k in geom's layout and dtype. */
 int nabla_pool(const nabla_geom* geom, const void* q, const void* k,
                float* qbar, float* kbar, void* stream);
 
@@ -225,7 +231,7 @@ int nabla_attn_fwd_vt(const nabla_geom* geom, const void* q, const void* k,
  *              order (pad slots included) its q, k and v rows of every head
  *   q, k       out, bf16 [B, heads, nb * 64, d]: copies, blocked layout
  *   vt         out, bf16 [B, heads, nb, d, 64]: as nabla_transpose_v of v
- *   qbar, kbar out, float32 [B, heads, nb, d]: bit-identical to nabla_pool
+ *   qbar, kbar out, float32, layouts as for nabla_pool: bit-identical to nabla_pool
  *              of q and k (means over the valid tokens; pad slots ignored)
  * Bit-exact otherwise. */
 int nabla_qkv_split(const nabla_geom* geom, const void* qkv, void* q, void* k,

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, f"{name} not exported"
         assert getattr(lib, name) is not None
-    assert lib.nabla_abi_version() == 3
+    assert lib.nabla_abi_version() == 4
 
 
 def G(**kw):
@@ -188,3 +188,20 @@ def test_probe_library_exports():
     lib.nabla_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                           ctypes.c_void_p]
     assert lib.nabla_probe_mfma_bf16(0, 1, FAKE, None) == -1
+
+
+def test_kbar_untile_follows_the_header_order():
+    """kbar_untile inverts the tiled order documented in include/nabla.h:
+    block 16 j + i, channel c at 16 j d + ((c / 16) * 4 + (c / 4) % 4) * 64 + 4 i + c % 4."""
+    import torch
+    from block_sparse_attention_flatten_amd.api import kbar_untile
+    for nb, d in ((37, 64), (48, 128)):
+        nb16 = -(-nb // 16) * 16
+        flat = torch.full((nb16 * d,), -1.0, dtype=torch.float64)
+        for row in range(nb):
+            for c in range(d):
+                off = (row // 16) * 16 * d + ((c // 16) * 4 + (c // 4) % 4) * 64 + 4 * (row % 16) + c % 4
+                flat[off] = row * 1000 + c
+        got = kbar_untile(flat.view(1, 1, nb16, d), nb)[0, 0]
+        want = torch.arange(nb, dtype=torch.float64)[:, None] * 1000 + torch.arange(d)[None, :]
+        assert torch.equal(got, want)

@@ -100,8 +100,8 @@ def test_forward_and_backward_graph_replays_match_eager():
 
     def step():
         dev = q.device
-        qbar = torch.empty((B, h, nb, d), dtype=torch.float32, device=dev)
-        kbar = torch.empty_like(qbar)
+        qbar = torch.empty(nabla.qbar_shape(g), dtype=torch.float32, device=dev)
+        kbar = torch.empty(nabla.kbar_shape(g), dtype=torch.float32, device=dev)
         bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
         cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)
         rp = torch.empty((B * h, nb + 1), dtype=torch.int32, device=dev)
@@ -175,8 +175,8 @@ def test_noalloc_and_layer_calls_graph_replays_match_eager():
         qb = torch.empty(gb.tensor_shape(), dtype=torch.bfloat16, device=dev)
         kb = torch.empty_like(qb)
         vt = torch.empty(nabla.vt_shape(gb), dtype=torch.bfloat16, device=dev)
-        qbar = torch.empty((B, h, nb, d), dtype=torch.float32, device=dev)
-        kbar = torch.empty_like(qbar)
+        qbar = torch.empty(nabla.qbar_shape(g), dtype=torch.float32, device=dev)
+        kbar = torch.empty(nabla.kbar_shape(g), dtype=torch.float32, device=dev)
         bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
         cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)
         rp = torch.empty((B * h, nb + 1), dtype=torch.int32, device=dev)
