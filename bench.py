@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 720p]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-nabla_mask_build (pooling, mask and compressed lists) ->
-nabla_transpose_v -> nabla_attn_fwd_vt (float32 inputs: nabla_attn_fwd),
+nabla_pool -> nabla_mask -> nabla_compact (the calls of nabla_mask_build),
+with nabla_transpose_v on a second stream beside the mask and compaction ->
+nabla_attn_fwd_vt (float32 inputs: nabla_attn_fwd),
 called through the C ABI
 on torch's current stream, with the fractal flatten applied inside the
 pooling, transpose and attention loaders (inputs and output stay in the
@@ -605,20 +606,26 @@ def main():
             nabla.nabla_attn_fwd(g, q, k, v, rp, ci, scale, o, stream)
 
     # V^T is written on a second stream (default priority) beside the mask
-    # construction.  It starts once the previous step's attention (the last
-    # reader of V^T) is done.
+    # kernel and the compaction.  It starts after the step's pooling, which
+    # also orders it after the previous step's attention (the last reader of
+    # V^T).
     side = torch.cuda.Stream() if vt_path and not args.serial else None
     started, vt_done = torch.cuda.Event(), torch.cuda.Event()
 
     def step(marks=None):
         if marks is not None:
             marks[0].record(stream)
+        # the three calls of nabla_mask_build, with V^T's HBM stream started
+        # once pooling (the other HBM-bound stage) is done, beside the mask
+        # and the compaction
+        nabla.nabla_pool(g, q, k, qbar, kbar, stream)
         if side is not None:
             started.record(stream)
             side.wait_event(started)
             nabla.nabla_transpose_v(g, v, vt, side)
             vt_done.record(side)
-        nabla.nabla_mask_build(g, q, k, thr, sta, qbar, kbar, bits, cnt, None, rp, ci, stream)
+        nabla.nabla_mask(g, qbar, kbar, thr, sta, bits, cnt, None, stream)
+        nabla.nabla_compact(g, bits, cnt, rp, ci, stream)
         if side is not None:
             stream.wait_event(vt_done)
         elif vt_path:
