@@ -38,7 +38,8 @@
  *   - All pointers except `geom`, `sta` and `bytes`/`offsets` outputs are
  *     DEVICE pointers, allocated and owned by the caller.  The library
  *     allocates no memory and keeps no state between calls apart from the
- *     thread-local last HIP error.
+ *     thread-local last HIP error and, for nabla_forward_noalloc, its
+ *     static per-GPU scratch array and that array's device address.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on that stream and returns; it never synchronizes.
  *   - Return value: NABLA_OK (0) or a negative NABLA_E_* code.  All argument
