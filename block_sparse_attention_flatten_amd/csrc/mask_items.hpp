@@ -631,10 +631,18 @@ __device__ inline void compact_rows(const Geo& g, const CompactArgs& a, int64_t 
   if (lane == n - 1 && r0 + n == nb) rp[nb] = base + incl;   // the head's last row
   int32_t* out = a.col_idx + head * (int64_t)nb * nb;
   const int cap = nb * nb;
-  for (int ri = 0; ri < n; ++ri) {
+  // every row's words are loaded up front, so their latency is paid once
+  uint32_t w0s[kCompactRows], w1s[kCompactRows];
+#pragma unroll
+  for (int ri = 0; ri < kCompactRows; ++ri) {
     const uint32_t* wrow = a.bits + (head * nb + r0 + ri) * (int64_t)nw;
-    const uint32_t w0 = lane < nw ? wrow[lane] : 0u;
-    const uint32_t w1 = lane + 64 < nw ? wrow[lane + 64] : 0u;
+    w0s[ri] = ri < n && lane < nw ? wrow[lane] : 0u;
+    w1s[ri] = ri < n && lane + 64 < nw ? wrow[lane + 64] : 0u;
+  }
+#pragma unroll
+  for (int ri = 0; ri < kCompactRows; ++ri) {
+    if (ri >= n) break;
+    const uint32_t w0 = w0s[ri], w1 = w1s[ri];
     int pos = __builtin_amdgcn_readlane(start, ri);
     for (int c0 = 0; c0 < nb; c0 += 64) {
       const int k = c0 >> 5;         // words k, k + 1 cover blocks c0 .. c0 + 63
