@@ -156,15 +156,17 @@ def test_backward_max_blocks_sampled():
     _backward_sampled(synth.config("long", T=64, heads=2, thr=0.5), 2, 1, "max_blocks backward")
 
 
-def test_dense_720p_sampled():
-    """nabla_dense_attn_fwd at the 720p bench shape, all 40 heads on the GPU:
+@pytest.mark.parametrize("shape", ["720p", "max_blocks"])
+def test_dense_sampled(shape):
+    """nabla_dense_attn_fwd at the 720p bench shape (all 40 heads) and at 3840
+    blocks per head (64 frames at 720p, close to the 4096-block limit):
     sampled query blocks of sampled heads against the oracle's attention over
     every valid key (the all-kept mask), lse included."""
     import math
     import block_sparse_attention_flatten_amd as nabla
     from gpu_helpers import geom_of
-    cfg = synth.config("720p")
-    log(f"dense 720p: generating inputs {cfg}")
+    cfg = synth.config("720p") if shape == "720p" else synth.config("long", T=64, heads=2)
+    log(f"dense {shape}: generating inputs {cfg}")
     q, k, v = synth.make_qkv(cfg, device="cuda")
     g = geom_of(cfg, out_dtype=torch.float32)
     nb = g.nb
@@ -175,18 +177,18 @@ def test_dense_720p_sampled():
     lse = torch.empty(nabla.lse_shape(g), dtype=torch.float32, device="cuda")
     nabla.nabla_dense_attn_fwd(g, q, k, vt, scale, o, lse)
     torch.cuda.synchronize()
-    log("dense 720p: GPU done")
+    log(f"dense {shape}: GPU done")
     og = ogeom(cfg)
     valid = O.valid_tokens(og)
     full = np.ones((nb, nb), dtype=bool)
     for h in synth.sampled_heads(cfg):
         qb, kb, vb = (O.flatten(f64(x[0, h]), og) for x in (q, k, v))
-        rows = _sample_rows(cfg, nb)
+        rows = _sample_rows(cfg, nb) if shape == "720p" else [0, 1234, nb - 1]
         ref = O.block_sparse_attention(qb, kb, vb, full, valid, rows=rows)
         got = O.flatten(f64(o[0, h]), og)
         sel = np.zeros_like(valid)
         sel[rows] = valid[rows]
-        e = check_output(got[sel], ref[sel], cfg.torch_dtype, f"dense 720p h{h}")
+        e = check_output(got[sel], ref[sel], cfg.torch_dtype, f"dense {shape} h{h}")
         kv = kb[valid]
         lse_h = lse[0, h].cpu().numpy().astype(np.float64)
         for r in rows[:6]:
@@ -194,4 +196,4 @@ def test_dense_720p_sampled():
             m = s.max(1)
             want = m + np.log(np.exp(s - m[:, None]).sum(1))
             assert np.abs(lse_h[r][valid[r]] - want).max() < 1e-2
-        log(f"dense 720p h{h}: rows {len(rows)} max|err| {e[0]:.2e} mean|err| {e[1]:.2e}")
+        log(f"dense {shape} h{h}: rows {len(rows)} max|err| {e[0]:.2e} mean|err| {e[1]:.2e}")
