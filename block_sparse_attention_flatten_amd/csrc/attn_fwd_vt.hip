@@ -10,6 +10,12 @@
 // so every K / V^T tile of the union is brought on chip once for both.
 // Wavefronts 0-1 own the first query block, 2-3 the second, 32 queries each.
 //
+// Dense mode (nabla_dense_attn_fwd; full attention, the baseline the method's
+// speed-ups are quoted against -- gist.science page, experimental results 1):
+// the same loop with eight wavefronts serving four consecutive query blocks,
+// the schedule being every key block in order (no lists, no merge, no
+// skipped stage).
+//
 // Prologue: the two kept lists are merged into an LDS list of 16-bit
 // entries (block index | latent-edge block << 12 | in-first-list << 14 |
 // in-second-list << 15) via LDS bitmaps, so the main loop reads its schedule
