@@ -197,3 +197,73 @@ def test_dense_sampled(shape):
             want = m + np.log(np.exp(s - m[:, None]).sum(1))
             assert np.abs(lse_h[r][valid[r]] - want).max() < 1e-2
         log(f"dense {shape} h{h}: rows {len(rows)} max|err| {e[0]:.2e} mean|err| {e[1]:.2e}")
+
+
+def test_layer_720p_sampled():
+    """The DiT-layer path at the 720p shape, as bench.py's layer leg runs it:
+    QKV = X W_qkv (library GEMM, 80640 x 5120 x 15360), nabla_qkv_split, mask,
+    lists and attention on all 40 heads; for sampled heads the pooled means,
+    the mask (bit-exact outside band rows) and sampled query blocks of the
+    output against the oracle on the projected q, k, v."""
+    import math
+    import block_sparse_attention_flatten_amd as nabla
+    cfg = synth.config("720p")
+    B, h, d = cfg.batch, cfg.heads, cfg.head_dim
+    g = nabla.Geometry(B, h, cfg.T, cfg.H, cfg.W, d, torch.bfloat16, nabla.LAYOUT_BLOCKED,
+                       out_dtype=torch.float32)
+    nb, S, Dm = g.nb, g.nb * 64, h * d
+    dev = "cuda"
+    log("layer 720p: generating inputs")
+    field = synth.make_tensor(cfg, 0, device=dev)
+    xb = torch.zeros(g.tensor_shape(), dtype=torch.bfloat16, device=dev)
+    nabla.nabla_flatten(g.with_layout(nabla.LAYOUT_THW), field, xb)
+    X = xb.permute(0, 2, 3, 1, 4).reshape(B, S, Dm).contiguous()
+    del field, xb
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    Wqkv = (torch.randn(Dm, 3 * Dm, generator=gen, device=dev) / math.sqrt(Dm)).to(torch.bfloat16)
+    qkv = torch.matmul(X, Wqkv).view(nabla.qkv_shape(g))
+    del X
+    q = torch.empty(g.tensor_shape(), dtype=torch.bfloat16, device=dev)
+    k = torch.empty_like(q)
+    vt = torch.empty(nabla.vt_shape(g), dtype=torch.bfloat16, device=dev)
+    qbar = torch.empty(nabla.qbar_shape(g), dtype=torch.float32, device=dev)
+    kbar = torch.empty(nabla.kbar_shape(g), dtype=torch.float32, device=dev)
+    bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
+    abits = torch.empty_like(bits)
+    cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)
+    rp = torch.empty((B * h, nb + 1), dtype=torch.int32, device=dev)
+    ci = torch.empty((B * h, nb * nb), dtype=torch.int32, device=dev)
+    o = torch.empty(g.tensor_shape(), dtype=torch.float32, device=dev)
+    nabla.nabla_qkv_split(g, qkv, q, k, vt, qbar, kbar)
+    nabla.nabla_mask(g, qbar, kbar, cfg.thr, cfg.sta, bits, cnt, abits)
+    nabla.nabla_compact(g, bits, cnt, rp, ci)
+    nabla.nabla_attn_fwd_vt(g, q, k, vt, rp, ci, 1.0 / math.sqrt(d), o)
+    torch.cuda.synchronize()
+    log("layer 720p: GPU done")
+    og = ogeom(cfg)
+    valid = O.valid_tokens(og)
+    kb_rows = nabla.kbar_untile(kbar, nb)
+    v = qkv[0, :, 2]                                          # [S, h, d], token-major
+    for hh in synth.sampled_heads(cfg)[:2]:
+        qh = f64(q[0, hh]).reshape(nb, 64, d)
+        kh = f64(k[0, hh]).reshape(nb, 64, d)
+        vh = f64(v[:, hh]).reshape(nb, 64, d)
+        qb_, kb_ = O.pool(qh, valid), O.pool(kh, valid)
+        for got, want, x in ((f64(qbar[0, hh]), qb_, qh), (f64(kb_rows[0, hh]), kb_, kh)):
+            assert np.abs(got - want).max() <= 64 * 2.0 ** -24 * np.abs(x).max()
+        m, m_ad, p = O.nabla_mask(qb_, kb_, cfg.thr, og, cfg.sta)
+        band_a, band_b = O.band_rows(p, m_ad, cfg.thr, 1e-5)
+        ref = dict(mask=m, mask_adaptive=m_ad, p=p, band=band_a | band_b, valid=valid)
+        union = unpack_bits(bits[0, hh], nb)
+        adapt = unpack_bits(abits[0, hh], nb)
+        nbnd, ndf = check_mask_rows(union, adapt, ref, cfg.thr, f"layer 720p h{hh}")
+        mm = gpu_mask_for_oracle(ref, union)
+        rows = sorted(set(_sample_rows(cfg, nb)) | set(np.flatnonzero((mm != m).any(1)).tolist()))
+        ob = O.block_sparse_attention(qh, kh, vh, mm, valid, rows=rows)
+        got = f64(o[0, hh]).reshape(nb, 64, d)
+        sel = np.zeros_like(valid)
+        sel[rows] = valid[rows]
+        e = check_output(got[sel], ob[sel], torch.bfloat16, f"layer 720p h{hh}")
+        log(f"layer 720p h{hh}: sparsity {1 - union.mean():.3f} band {nbnd} diff {ndf} "
+            f"rows {len(rows)} max|err| {e[0]:.2e} mean|err| {e[1]:.2e}")
