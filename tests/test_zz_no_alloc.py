@@ -1,7 +1,7 @@
 """nabla_forward_noalloc (library-owned scratch array, allocates nothing)
 against nabla_forward (caller workspace), both through the C ABI: outputs
 equal bit for bit, on calls in a row where the second input is smaller than
-the first, then a float32 call."""
+the first, then a larger batched one and a float32 call."""
 import math
 
 import pytest
@@ -18,6 +18,9 @@ CASES = [
     synth.config("720p", heads=20),
     # smaller, with ragged edge blocks
     synth.config("small", heads=3, T=3, H=20, W=28),
+    # batch 2 x 6 heads at the 720p shape: a pass boundary inside the second
+    # batch entry's heads
+    synth.config("720p", batch=2, heads=6),
     # float32 inputs (no V^T part), no STA window
     synth.config("tiny"),
 ]
