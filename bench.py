@@ -234,7 +234,7 @@ def layer_leg(torch, nabla, cfg, g, x_field, thr, sta, scale, time_call, dev):
     Wo = (torch.randn(D, D, generator=gen, device=dev) / math.sqrt(D)).to(torch.bfloat16)
     gb = g.with_layout(nabla.LAYOUT_BLOCKED)
     qbar = torch.empty(nabla.qbar_shape(gb), dtype=torch.float32, device=dev)
-    kbar = torch.empty(nabla.kbar_shape(gb), dtype=torch.float32, device=dev)
+    kbar = torch.empty(nabla.kbar_shape(gb), dtype=nabla.KBAR_DTYPE, device=dev)
     bits = torch.empty((1, h, nb, g.nw), dtype=torch.int32, device=dev)
     cnt = torch.empty((1, h, nb), dtype=torch.int32, device=dev)
     rp = torch.empty((h, nb + 1), dtype=torch.int32, device=dev)
@@ -493,7 +493,7 @@ def config_summary(torch, nabla, synth, name, time_call, stream):
     B, h, nb, d = cfg.batch, cfg.heads, g.nb, cfg.head_dim
     dev = q.device
     qbar = torch.empty(nabla.qbar_shape(g), dtype=torch.float32, device=dev)
-    kbar = torch.empty(nabla.kbar_shape(g), dtype=torch.float32, device=dev)
+    kbar = torch.empty(nabla.kbar_shape(g), dtype=nabla.KBAR_DTYPE, device=dev)
     bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
     abits = torch.empty_like(bits)
     cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)
@@ -586,7 +586,7 @@ def main():
     B, h, nb, d = cfg.batch, cfg.heads, g.nb, cfg.head_dim
     dev = q.device
     qbar = torch.empty(nabla.qbar_shape(g), dtype=torch.float32, device=dev)
-    kbar = torch.empty(nabla.kbar_shape(g), dtype=torch.float32, device=dev)
+    kbar = torch.empty(nabla.kbar_shape(g), dtype=nabla.KBAR_DTYPE, device=dev)
     bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)
     rp = torch.empty((B * h, nb + 1), dtype=torch.int32, device=dev)

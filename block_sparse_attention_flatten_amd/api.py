@@ -5,8 +5,9 @@ kernels behind include/nabla.h; PyTorch provides device memory and the stream.
 Tensor layouts are those of the C header:
   THW      [B, heads, T, H, W, d]      (natural latent order, valid tokens)
   BLOCKED  [B, heads, nb, 64, d]       (fractal-flattened, padded)
-  qbar float32 [B, heads, nb, d]; kbar float32 [B, heads, nb16, d] in the
-  header's tiled order (nb16 = nb rounded up to 16; kbar_shape, kbar_untile);
+  qbar float32 [B, heads, nb, d]; kbar bf16 [B, heads, nb16, 3 d]: each mean
+  as three exact bf16 parts in the header's tiled order (nb16 = nb rounded up
+  to 16; kbar_shape, KBAR_DTYPE, kbar_untile);
   mask words uint32 stored in int32
   tensors [B, heads, nb, ceil(nb/32)]; row counts int32 [B, heads, nb];
   row_ptr int32 [B*heads, nb+1]; col_idx int32 [B*heads, nb*nb].
@@ -27,7 +28,7 @@ __all__ = [
     "NablaError", "Geometry", "nabla_num_blocks", "nabla_flatten", "nabla_unflatten",
     "nabla_pool", "nabla_mask", "nabla_compact", "nabla_mask_build", "nabla_attn_fwd",
     "nabla_transpose_v", "nabla_dense_attn_fwd", "nabla_qkv_split", "qkv_shape", "qbar_shape",
-    "kbar_shape", "kbar_untile",
+    "kbar_shape", "kbar_untile", "KBAR_DTYPE",
     "nabla_attn_fwd_vt", "nabla_forward_workspace_size", "nabla_forward", "nabla_forward_noalloc",
     "nabla_status_string",
     "nabla_attn_fwd_lse", "nabla_attn_fwd_vt_lse", "nabla_mask_transpose", "nabla_attn_bwd_dq",
@@ -169,18 +170,27 @@ def qbar_shape(g: Geometry) -> Tuple[int, ...]:
     return (g.batch, g.heads, g.nb, g.head_dim)
 
 
+# element type of the pooled keys (three bf16 parts per float32 mean)
+KBAR_DTYPE = torch.bfloat16
+
+
 def kbar_shape(g: Geometry) -> Tuple[int, ...]:
-    """Pooled keys [B, heads, nb16, d] float32, nb16 = nb rounded up to 16
-    (the tiled order of the header)."""
-    return (g.batch, g.heads, -(-g.nb // 16) * 16, g.head_dim)
+    """Pooled keys [B, heads, nb16, 3 d] of KBAR_DTYPE, nb16 = nb rounded up
+    to 16: the 3 nb16 d bf16 parts of a head in the header's tiled order (the
+    shape only sizes the buffer)."""
+    return (g.batch, g.heads, -(-g.nb // 16) * 16, 3 * g.head_dim)
 
 
 def kbar_untile(kbar: torch.Tensor, nb: int) -> torch.Tensor:
-    """Pooled keys in the tiled order -> [.., nb, d] rows (a copy; layout
-    helper for inspection, no arithmetic)."""
-    *lead, nb16, d = kbar.shape
-    x = kbar.reshape(*lead, nb16 // 16, d // 16, 4, 16, 4)     # [tile, c/16, (c/4)%4, i, c%4]
-    x = x.movedim(-2, -4)                                      # [tile, i, c/16, (c/4)%4, c%4]
+    """Pooled keys in their split, tiled encoding -> float32 [.., nb, d] rows
+    (a copy for inspection: each mean is h + m + l of its three parts, summed
+    in float32 as (h + m) + l, which gives the mean back exactly)."""
+    *lead, nb16, d3 = kbar.shape
+    d = d3 // 3
+    # [tile j, k-step t, part p, channel group g, row i, channel e]
+    x = kbar.reshape(*lead, nb16 // 16, d // 32, 3, 4, 16, 8).to(torch.float32)
+    x = (x[..., 0, :, :, :] + x[..., 1, :, :, :]) + x[..., 2, :, :, :]   # [j, t, g, i, e]
+    x = x.movedim(-2, -4)                                                 # [j, i, t, g, e]
     return x.reshape(*lead, nb16, d)[..., :nb, :]
 
 
@@ -189,7 +199,7 @@ def nabla_pool(g: Geometry, q, k, qbar, kbar, stream=None) -> None:
     _check(_lib.load().nabla_pool(
         ctypes.byref(g.c()), _ptr(q, "q", shp, g.dtype), _ptr(k, "k", shp, g.dtype),
         _ptr(qbar, "qbar", qbar_shape(g), torch.float32),
-        _ptr(kbar, "kbar", kbar_shape(g), torch.float32),
+        _ptr(kbar, "kbar", kbar_shape(g), KBAR_DTYPE),
         _stream(stream)), "nabla_pool")
 
 
@@ -198,7 +208,7 @@ def nabla_mask(g: Geometry, qbar, kbar, thr: float, sta, mask_bits, row_count,
     mshape = (g.batch, g.heads, g.nb, g.nw)
     _check(_lib.load().nabla_mask(
         ctypes.byref(g.c()), _ptr(qbar, "qbar", qbar_shape(g), torch.float32),
-        _ptr(kbar, "kbar", kbar_shape(g), torch.float32), float(thr), _sta(sta),
+        _ptr(kbar, "kbar", kbar_shape(g), KBAR_DTYPE), float(thr), _sta(sta),
         _ptr(mask_bits, "mask_bits", mshape, torch.int32),
         _ptr(row_count, "row_count", (g.batch, g.heads, g.nb), torch.int32),
         _ptr(adaptive_bits, "adaptive_bits", mshape, torch.int32), _stream(stream)),
@@ -224,7 +234,7 @@ def nabla_mask_build(g: Geometry, q, k, thr: float, sta, qbar, kbar, mask_bits, 
     _check(_lib.load().nabla_mask_build(
         ctypes.byref(g.c()), _ptr(q, "q", shp, g.dtype), _ptr(k, "k", shp, g.dtype), float(thr),
         _sta(sta), _ptr(qbar, "qbar", qbar_shape(g), torch.float32),
-        _ptr(kbar, "kbar", kbar_shape(g), torch.float32),
+        _ptr(kbar, "kbar", kbar_shape(g), KBAR_DTYPE),
         _ptr(mask_bits, "mask_bits", mshape, torch.int32),
         _ptr(row_count, "row_count", (g.batch, g.heads, g.nb), torch.int32),
         _ptr(adaptive_bits, "adaptive_bits", mshape, torch.int32),
@@ -278,7 +288,7 @@ def nabla_qkv_split(g: Geometry, qkv, q, k, vt, qbar, kbar, stream=None) -> None
         ctypes.byref(g.c()), _ptr(qkv, "qkv", qkv_shape(g), g.dtype),
         _ptr(q, "q", shp, g.dtype), _ptr(k, "k", shp, g.dtype),
         _ptr(vt, "vt", vt_shape(g), g.dtype), _ptr(qbar, "qbar", qbar_shape(g), torch.float32),
-        _ptr(kbar, "kbar", kbar_shape(g), torch.float32), _stream(stream)), "nabla_qkv_split")
+        _ptr(kbar, "kbar", kbar_shape(g), KBAR_DTYPE), _stream(stream)), "nabla_qkv_split")
 
 
 def nabla_dense_attn_fwd(g: Geometry, q, k, vt, scale: float, o, lse=None,
@@ -429,7 +439,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, thr: float,
     return ForwardResult(
         o=o,
         qbar=part(0, torch.float32, (B, h, g.nb, d)),
-        kbar=part(1, torch.float32, kbar_shape(g)),
+        kbar=part(1, KBAR_DTYPE, kbar_shape(g)),
         mask_bits=part(2, torch.int32, (B, h, g.nb, g.nw)),
         row_count=part(3, torch.int32, (B, h, g.nb)),
         row_ptr=part(4, torch.int32, (bh, g.nb + 1)),
@@ -487,7 +497,7 @@ class NablaAttention(torch.autograd.Function):
         dev = q.device
         nb = g.nb
         qbar = torch.empty(qbar_shape(g), dtype=torch.float32, device=dev)
-        kbar = torch.empty(kbar_shape(g), dtype=torch.float32, device=dev)
+        kbar = torch.empty(kbar_shape(g), dtype=KBAR_DTYPE, device=dev)
         bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
         cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)
         rp = torch.empty((B * h, nb + 1), dtype=torch.int32, device=dev)

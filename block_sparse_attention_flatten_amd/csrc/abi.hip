@@ -87,7 +87,7 @@ void workspace_parts(const Geo& g, bool bf16, size_t off[kWsParts], size_t* tota
   const size_t bh = (size_t)g.bh, nb = (size_t)g.nb, nw = (nb + 31) / 32;
   const size_t sizes[kWsParts] = {
       bh * nb * g.d * sizeof(float),        // qbar
-      bh * (size_t)nabla::kbar_rows(g.nb) * g.d * sizeof(float),   // kbar (tiled)
+      bh * (size_t)nabla::kbar_head_elems(g.nb, g.d) * 2,   // kbar (split parts, tiled)
       bh * nb * nw * sizeof(uint32_t),      // mask bits
       bh * nb * sizeof(int32_t),            // row counts
       bh * (nb + 1) * sizeof(int32_t),      // row_ptr
@@ -126,7 +126,7 @@ hipError_t forward_pass(const Geo& g, bool bf16, bool out_bf16, const void* q, c
                         const void* v, float thr, const int win[3], float scale, void* o,
                         char* ws, const size_t off[kWsParts], hipStream_t s) {
   float* qbar = (float*)(ws + off[0]);
-  float* kbar = (float*)(ws + off[1]);
+  __bf16* kbar = (__bf16*)(ws + off[1]);
   uint32_t* bits = (uint32_t*)(ws + off[2]);
   int32_t* cnt = (int32_t*)(ws + off[3]);
   int32_t* rp = (int32_t*)(ws + off[4]);
@@ -273,7 +273,7 @@ int nabla_unflatten(const nabla_geom* geom, const void* x_blocked, void* x, void
   return hip_status(nabla::launch_flatten(g, eb, x_blocked, x, true, as_stream(stream)));
 }
 
-int nabla_pool(const nabla_geom* geom, const void* q, const void* k, float* qbar, float* kbar,
+int nabla_pool(const nabla_geom* geom, const void* q, const void* k, float* qbar, void* kbar,
                void* stream) {
   Geo g;
   bool empty;
@@ -281,11 +281,11 @@ int nabla_pool(const nabla_geom* geom, const void* q, const void* k, float* qbar
   if (st != NABLA_OK) return st;
   if (empty) return NABLA_OK;
   if (q == nullptr || k == nullptr || qbar == nullptr || kbar == nullptr) return NABLA_E_NULL;
-  return hip_status(nabla::launch_pool(g, geom->dtype == NABLA_DTYPE_BF16, q, k, qbar, kbar,
-                                       as_stream(stream)));
+  return hip_status(nabla::launch_pool(g, geom->dtype == NABLA_DTYPE_BF16, q, k, qbar,
+                                       (__bf16*)kbar, as_stream(stream)));
 }
 
-int nabla_mask(const nabla_geom* geom, const float* qbar, const float* kbar, float thr,
+int nabla_mask(const nabla_geom* geom, const float* qbar, const void* kbar, float thr,
                const int32_t* sta, uint32_t* mask_bits, int32_t* row_count,
                uint32_t* adaptive_bits, void* stream) {
   Geo g;
@@ -299,8 +299,8 @@ int nabla_mask(const nabla_geom* geom, const float* qbar, const float* kbar, flo
   if (empty) return NABLA_OK;
   if (qbar == nullptr || kbar == nullptr || mask_bits == nullptr || row_count == nullptr)
     return NABLA_E_NULL;
-  return hip_status(nabla::launch_mask(g, qbar, kbar, thr, win, mask_bits, row_count,
-                                       adaptive_bits, as_stream(stream)));
+  return hip_status(nabla::launch_mask(g, qbar, (const __bf16*)kbar, thr, win, mask_bits,
+                                       row_count, adaptive_bits, as_stream(stream)));
 }
 
 int nabla_compact(const nabla_geom* geom, const uint32_t* mask_bits, const int32_t* row_count,
@@ -317,7 +317,7 @@ int nabla_compact(const nabla_geom* geom, const uint32_t* mask_bits, const int32
 }
 
 int nabla_mask_build(const nabla_geom* geom, const void* q, const void* k, float thr,
-                     const int32_t* sta, float* qbar, float* kbar, uint32_t* mask_bits,
+                     const int32_t* sta, float* qbar, void* kbar, uint32_t* mask_bits,
                      int32_t* row_count, uint32_t* adaptive_bits, int32_t* row_ptr,
                      int32_t* col_idx, void* stream) {
   Geo g;
@@ -332,8 +332,8 @@ int nabla_mask_build(const nabla_geom* geom, const void* q, const void* k, float
   if (q == nullptr || k == nullptr || qbar == nullptr || kbar == nullptr ||
       mask_bits == nullptr || row_count == nullptr || row_ptr == nullptr || col_idx == nullptr)
     return NABLA_E_NULL;
-  return hip_status(nabla::launch_mask_build(g, geom->dtype == NABLA_DTYPE_BF16, q, k, qbar, kbar,
-                                             thr, win, mask_bits, row_count, adaptive_bits,
+  return hip_status(nabla::launch_mask_build(g, geom->dtype == NABLA_DTYPE_BF16, q, k, qbar,
+                                             (__bf16*)kbar, thr, win, mask_bits, row_count, adaptive_bits,
                                              row_ptr, col_idx, as_stream(stream)));
 }
 
@@ -367,7 +367,7 @@ int nabla_attn_fwd_vt(const nabla_geom* geom, const void* q, const void* k, cons
 }
 
 int nabla_qkv_split(const nabla_geom* geom, const void* qkv, void* q, void* k, void* vt,
-                    float* qbar, float* kbar, void* stream) {
+                    float* qbar, void* kbar, void* stream) {
   Geo g;
   bool empty;
   const int st = make_geo(geom, true, &g, &empty);
@@ -380,7 +380,7 @@ int nabla_qkv_split(const nabla_geom* geom, const void* qkv, void* q, void* k, v
       kbar == nullptr)
     return NABLA_E_NULL;
   return hip_status(nabla::launch_qkv_split(g, (int)geom->batch, (int)geom->heads, qkv, q, k, vt,
-                                            qbar, kbar, as_stream(stream)));
+                                            qbar, (__bf16*)kbar, as_stream(stream)));
 }
 
 int nabla_dense_attn_fwd(const nabla_geom* geom, const void* q, const void* k, const void* vt,

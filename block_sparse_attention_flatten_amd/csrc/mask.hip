@@ -4,8 +4,9 @@
 // standalone call on pooled inputs (nabla_mask) and as the middle step of
 // the mask construction call (nabla_mask_build: pooling, mask, lists).
 //
-// A row group is R rows of one head: their scores on fp32 matrix cores
-// staged in an LDS tile (score_tiles), then one wavefront per row for
+// A row group is R rows of one head: their scores (float32 accuracy from
+// split bf16 products on the matrix cores) staged in an LDS tile
+// (score_tiles), then one wavefront per row for
 // softmax, CDF cut and STA union (cut_rows); see mask_items.hpp.
 //
 // The mask construction call runs pooling, mask and compaction as three
@@ -60,7 +61,7 @@ hipError_t dispatch_shape(int nb, const F& f) {
   return f.template operator()<D, 8, 8, 64>();
 }
 
-MaskArgs mask_args(const Geo& g, const float* qbar, const float* kbar, float thr,
+MaskArgs mask_args(const Geo& g, const float* qbar, const __bf16* kbar, float thr,
                    const int sta[3], uint32_t* bits, int32_t* cnt, uint32_t* abits) {
   MaskArgs a;
   a.qbar = qbar;
@@ -92,7 +93,7 @@ struct MaskRun {
 
 }  // namespace
 
-hipError_t launch_mask(const Geo& g, const float* qbar, const float* kbar, float thr,
+hipError_t launch_mask(const Geo& g, const float* qbar, const __bf16* kbar, float thr,
                        const int sta[3], uint32_t* bits, int32_t* cnt, uint32_t* abits,
                        hipStream_t s) {
   const MaskArgs a = mask_args(g, qbar, kbar, thr, sta, bits, cnt, abits);
@@ -101,7 +102,7 @@ hipError_t launch_mask(const Geo& g, const float* qbar, const float* kbar, float
 }
 
 hipError_t launch_mask_build(const Geo& g, bool bf16, const void* q, const void* k, float* qbar,
-                             float* kbar, float thr, const int sta[3], uint32_t* bits,
+                             __bf16* kbar, float thr, const int sta[3], uint32_t* bits,
                              int32_t* cnt, uint32_t* abits, int32_t* row_ptr, int32_t* col_idx,
                              hipStream_t s) {
   hipError_t e = launch_pool(g, bf16, q, k, qbar, kbar, s);

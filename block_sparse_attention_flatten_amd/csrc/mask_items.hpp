@@ -6,9 +6,9 @@
 //     Neighborhood Adaptive Block-Level Attention", gist.science,
 //     Methodology: downsampling);
 //   * score_tiles / cut_rows - a group of R rows of one head: reduced scores
-//     on fp32 matrix cores staged in LDS, then softmax, CDF cut and STA union
-//     per row (Methodology: reduced attention, CDF thresholding, hybrid
-//     integration with STA);
+//     (float32 accuracy from split bf16 products) staged in LDS, then
+//     softmax, CDF cut and STA union per row (Methodology: reduced attention,
+//     CDF thresholding, hybrid integration with STA);
 //   * compact_rows - rows of a mask expanded into the compressed kept lists
 //     (lsdiaocha.cn article on NABLA, sec. 5: compressed sparse storage).
 // Because each piece is one wavefront's work, a kernel may hand the pieces to
@@ -159,18 +159,36 @@ __device__ inline void pool_block(const Geo& g, const T* x, int b,
   for (int e = 0; e < S::kElems; ++e) mean[e] *= inv;
 }
 
-// Store pool_block's result as row `row` of a head's pooled keys in the
-// tiled order (kbar_offset): four consecutive channels stay contiguous.
+// Store pool_block's result as row `row` of a head's pooled keys: each mean
+// as its three exact bf16 parts, in the tiled order of kbar_offset (the
+// lane's kElems consecutive channels are consecutive there).
+__device__ inline void split3(float x, __bf16& h, __bf16& m, __bf16& l) {
+  h = (__bf16)x;
+  const float r = x - (float)h;     // exact
+  m = (__bf16)r;
+  l = (__bf16)(r - (float)m);       // exact, and exactly a bf16
+}
 template <typename T, int D>
 __device__ inline void store_mean_tiled(const float (&mean)[PoolShape<T, D>::kElems],
-                                        float* head_base, int row) {
+                                        __bf16* head_base, int row) {
   using S = PoolShape<T, D>;
+  constexpr int E = S::kElems;
+  typedef __attribute__((ext_vector_type(E))) __bf16 part_t;
   const int lane = threadIdx.x & 63;
   if (lane < S::kLanesPerRow) {
+    part_t h, m, l;
 #pragma unroll
-    for (int e = 0; e < S::kElems; e += 4)
-      *(f32x4*)(head_base + kbar_offset(row, lane * S::kElems + e, D)) =
-          f32x4{mean[e], mean[e + 1], mean[e + 2], mean[e + 3]};
+    for (int e = 0; e < E; ++e) {
+      __bf16 a, b, c;
+      split3(mean[e], a, b, c);
+      h[e] = a;
+      m[e] = b;
+      l[e] = c;
+    }
+    const int c0 = lane * E;
+    *(part_t*)(head_base + kbar_offset(row, c0, 0, D)) = h;
+    *(part_t*)(head_base + kbar_offset(row, c0, 1, D)) = m;
+    *(part_t*)(head_base + kbar_offset(row, c0, 2, D)) = l;
   }
 }
 
@@ -432,7 +450,7 @@ __device__ inline void cdf_cut(const float (&e)[J], float xlo, int nb, float Z, 
 // ---------------------------------------------------------------------------
 struct MaskArgs {
   const float* qbar;    // [bh, nb, d]
-  const float* kbar;    // [bh, nb, d]
+  const __bf16* kbar;   // per head kbar_head_elems(nb, d): split parts, tiled
   float scale;          // log2(e) / sqrt(d): scores carried in the exp2 domain
   float thr;
   int rt, rh, rw;       // STA half-widths; rt < 0: no window
@@ -455,83 +473,109 @@ __host__ __device__ inline int mask_stride(int nb) {
 
 // Scores of one row group (rows r0 .. r0 + R - 1 of a head) for the column
 // tiles ct = first, first + step, ... (16 key blocks each) into the LDS
-// tile S (R x a.stride floats), on fp32 matrix cores: C[16 rows][16 cols]
-// per tile, scaled into the exp2 domain.  One wavefront; the next tile's K
-// rows are loaded while the current one is multiplied.  The wavefront walks
-// its tiles starting at position rot (mod their count): workgroups that work
-// on the same head at the same time then read different K rows, instead of
-// all hitting the same lines (and L2 channel) at once.
+// tile S (R x a.stride floats), scaled into the exp2 domain.  One wavefront.
+//
+// q.k in float32 accuracy on bf16 matrix cores: with q = qh + qm + ql and
+// k = kh + km + kl the exact three-part splits of the float32 means, the
+// products qh.kh, qh.km, qm.kh, qh.kl, qm.km and ql.kh are formed by
+// v_mfma_f32_16x16x32_bf16 (bf16 x bf16 products are exact in float32); the
+// three dropped ones are below 2^-25 of |q_i k_i| each.  Two accumulators
+// take alternate products, so consecutive matrix instructions do not wait on
+// each other, and the order is fixed.
+//
+// The query parts are split once per group from the float32 rows; the key
+// parts come pre-split in their tiled order (kbar_offset) through a buffer
+// descriptor, each 16-byte-per-lane load one contiguous kilobyte.  The next
+// tile's loads of a k-step are issued as soon as that k-step's products have
+// read their operands, so up to a tile of loads is in flight.  The
+// wavefront walks its tiles starting at position rot (mod their count):
+// workgroups working on the same head at once then read different K rows
+// instead of all hitting the same lines (and L2 channel) together.
 template <int D, int R>
 __device__ inline void score_tiles(const Geo& g, const MaskArgs& a, int64_t head, int r0,
                                    float* S, int first, int step, int rot) {
+  constexpr int KT = D / 32;          // k-steps of 32 channels
   const int nb = g.nb;
   const int lane = threadIdx.x & 63;
-  const float* Kh = a.kbar + head * kbar_rows(nb) * D;   // tiled (kbar_offset)
+  const __bf16* Kh = a.kbar + head * kbar_head_elems(nb, D);
   const float* Qh = a.qbar + head * nb * D;
   const int i16 = lane & 15;          // A row / B column of this lane
-  const int g4 = lane >> 4;           // k sub-index
+  const int g4 = lane >> 4;           // channel group of 8 within a k-step
   const int qrow = r0 + i16;
   const bool arow = i16 < R && qrow < nb;
   const int ntiles = (nb + 15) >> 4;
   if (first >= ntiles) return;
 
-  // A operand: the group's pooled query rows.  The contraction index is
-  // permuted consistently for A and B: in step 4t+u this lane supplies
-  // element 16t + 4*g4 + u of its row.
-  f32x4 aop[D / 16];
+  // A operand: row i16's channels 32 t + 8 g4 .. + 7, as three parts
+  bf16x8 ah[KT], am[KT], al[KT];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t)
-    aop[t] = arow ? *(const f32x4*)(Qh + (int64_t)qrow * D + 16 * t + 4 * g4)
-                  : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < KT; ++t) {
+    const float* src = Qh + (int64_t)qrow * D + 32 * t + 8 * g4;
+    const f32x4 x0 = arow ? *(const f32x4*)src : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 x1 = arow ? *(const f32x4*)(src + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16 h, m, l;
+      split3(e < 4 ? x0[e] : x1[e - 4], h, m, l);
+      ah[t][e] = h;
+      am[t][e] = m;
+      al[t][e] = l;
+    }
+  }
 
-  // K rows through a buffer descriptor over the head's pooled keys.  In
-  // their tiled order, load t of a tile gives lane l the 16 bytes at
-  // (64 t + l) * 16: row i16, channels 16t + 4 g4 .. + 3, one contiguous
-  // kilobyte per load.  Lanes of rows past the last block load zeros.
-  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kh, (uint32_t)(kbar_rows(nb) * D * 4));
+  // B operand: k-step t of tile ct is 3 KB at ct * KT * 3 KB + t * 3 KB (one
+  // kilobyte per part); lanes of rows past the last block load zeros
+  const __amdgpu_buffer_rsrc_t krs =
+      buffer_rsrc(Kh, (uint32_t)(kbar_head_elems(nb, D) * (int64_t)sizeof(__bf16)));
   const uint32_t lane_off = (uint32_t)(lane * 16);
-  auto load_b = [&](int ct, f32x4 (&bv)[D / 16]) {
+  auto load_kstep = [&](int ct, int t, bf16x8 (&b)[3]) {
     const uint32_t voff = ct * 16 + i16 < nb ? lane_off : 0x80000000u;
     // the tile offset is wavefront-uniform; say so, or the compiler wraps
     // each load in a loop over the distinct values it thinks lanes hold
-    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(ct * 16 * D * 4);
+    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(ct * KT * 3 * 1024);
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-      bv[t] = __builtin_bit_cast(
-          f32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff + 1024u * t, soff, 0));
+    for (int p = 0; p < 3; ++p)
+      b[p] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                            krs, voff + 1024u * (3 * t + p), soff, 0));
   };
-  // two accumulators (even and odd k-chunks) so consecutive matrix
-  // instructions do not wait on each other; one fixed summation order
-  auto tile = [&](int ct, const f32x4 (&bv)[D / 16]) {
+  const int n = (ntiles - first + step - 1) / step;   // this wavefront's tiles
+  const int i = rot % n;
+  auto tile_at = [&](int k) {          // k-th tile of the rotated walk
+    const int m = i + k;
+    return first + step * (m >= n ? m - n : m);
+  };
+  bf16x8 kb[KT][3];
+  {
+    const int ct = tile_at(0);
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      load_kstep(ct, t, kb[t]);
+      __builtin_amdgcn_sched_barrier(0);   // same load order as in the loop
+    }
+  }
+  for (int k = 0; k < n; ++k) {
+    const int ct = tile_at(k);
+    // after the last tile, the loads repeat it (unused): the load count per
+    // iteration stays fixed, so the waits before each k-step stay exact
+    const int nxt = k + 1 < n ? tile_at(k + 1) : ct;
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < D / 16; t += 2)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[t][u], bv[t][u], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[t + 1][u], bv[t + 1][u], acc1, 0, 0, 0);
-      }
+    for (int t = 0; t < KT; ++t) {
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[t], kb[t][0], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[t], kb[t][1], acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[t], kb[t][0], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[t], kb[t][2], acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[t], kb[t][1], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[t], kb[t][0], acc1, 0, 0, 0);
+      load_kstep(nxt, t, kb[t]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // acc[r] = C[4*g4 + r][i16]
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * g4 + r;
       if (row < R) S[row * a.stride + ct * 16 + i16] = (acc0[r] + acc1[r]) * a.scale;
     }
-  };
-  const int n = (ntiles - first + step - 1) / step;   // this wavefront's tiles
-  int i = rot % n;
-  auto tile_at = [&](int k) {          // k-th tile of the rotated walk
-    const int m = i + k;
-    return first + step * (m >= n ? m - n : m);
-  };
-  f32x4 b0[D / 16], b1[D / 16];
-  load_b(tile_at(0), b0);
-  for (int k = 0; k < n; k += 2) {
-    if (k + 1 < n) load_b(tile_at(k + 1), b1);
-    tile(tile_at(k), b0);
-    if (k + 1 >= n) break;
-    if (k + 2 < n) load_b(tile_at(k + 2), b0);
-    tile(tile_at(k + 1), b1);
   }
 }
 

@@ -49,12 +49,23 @@ struct Geo {
   Recip gw_r;        // division by gw
 };
 
-// Pooled keys are stored in tiles of 16 blocks, in the order the mask
-// kernel's matrix-core operand loads read them: float offset of (block row,
-// channel c) within a head, and the padded row count of a head.
+// Pooled keys.  Each float32 mean x is stored exactly as three bf16 parts
+// h = bf16(x), m = bf16(x - h), l = x - h - m (x - h and x - h - m are exact
+// in float32, and the last one fits in bf16), so h + m + l == x, and the mask
+// kernel forms q.k from six bf16 products.  The parts sit in tiles of 16
+// blocks in the order of that kernel's matrix-core operand loads: within
+// tile j, k-step t (channels 32 t .. 32 t + 31) and part p, lane 16 g + i of a
+// wavefront reads the 16 bytes of block 16 j + i, channels 32 t + 8 g .. + 7,
+// so each load is one contiguous kilobyte.  Offset in bf16 elements within a
+// head, and the padded row count of a head:
 __host__ __device__ inline int kbar_rows(int nb) { return (nb + 15) & ~15; }
-__host__ __device__ inline int kbar_offset(int row, int c, int d) {
-  return (row >> 4) * 16 * d + (((c >> 4) << 2) + ((c >> 2) & 3)) * 64 + (row & 15) * 4 + (c & 3);
+__host__ __device__ inline int kbar_offset(int row, int c, int p, int d) {
+  return ((((row >> 4) * (d >> 5) + (c >> 5)) * 3 + p) * 64 + ((c >> 3) & 3) * 16 + (row & 15)) *
+             8 + (c & 7);
+}
+// bf16 elements of one head's pooled keys
+__host__ __device__ inline int64_t kbar_head_elems(int nb, int d) {
+  return (int64_t)kbar_rows(nb) * d * 3;
 }
 
 struct BlockCoord {
@@ -106,15 +117,15 @@ __device__ inline int block_row_step(const Geo& g) {
 hipError_t launch_flatten(const Geo& g, int elem_bytes, const void* src, void* dst, bool inverse,
                           hipStream_t s);
 hipError_t launch_pool(const Geo& g, bool bf16, const void* q, const void* k, float* qbar,
-                       float* kbar, hipStream_t s);
-hipError_t launch_mask(const Geo& g, const float* qbar, const float* kbar, float thr,
+                       __bf16* kbar, hipStream_t s);
+hipError_t launch_mask(const Geo& g, const float* qbar, const __bf16* kbar, float thr,
                        const int sta[3], uint32_t* bits, int32_t* cnt, uint32_t* abits,
                        hipStream_t s);
 hipError_t launch_compact(const Geo& g, const uint32_t* bits, const int32_t* cnt,
                           int32_t* row_ptr, int32_t* col_idx, hipStream_t s);
 // pool, mask and compact in order on one stream (mask.hip)
 hipError_t launch_mask_build(const Geo& g, bool bf16, const void* q, const void* k, float* qbar,
-                             float* kbar, float thr, const int sta[3], uint32_t* bits,
+                             __bf16* kbar, float thr, const int sta[3], uint32_t* bits,
                              int32_t* cnt, uint32_t* abits, int32_t* row_ptr, int32_t* col_idx,
                              hipStream_t s);
 // lse (nullable): float32 [bh, nb, 64] natural-log log-sum-exp of each query's
@@ -139,7 +150,7 @@ hipError_t launch_attn_fwd_vt(const Geo& g, bool out_bf16, const void* q, const 
                               const void* vt, const int32_t* row_ptr, const int32_t* col_idx,
                               float scale, void* o, float* lse, hipStream_t s);
 hipError_t launch_qkv_split(const Geo& g, int batch, int heads, const void* qkv, void* q, void* k,
-                            void* vt, float* qbar, float* kbar, hipStream_t s);
+                            void* vt, float* qbar, __bf16* kbar, hipStream_t s);
 hipError_t launch_attn_dense_vt(const Geo& g, bool out_bf16, const void* q, const void* k,
                                 const void* vt, float scale, void* o, float* lse,
                                 hipStream_t s);

@@ -8,7 +8,7 @@
 //   q, k   head-major copies in the blocked layout,
 //   V^T    the attention kernel's transposed V operand (as nabla_transpose_v),
 //   q̄, k̄   the means of the block's valid tokens (as nabla_pool, same bits
-//          and the same tiled order for k̄),
+//          and the same split, tiled encoding for k̄),
 // so pooling and the V transpose cost no pass of their own.
 //
 // One workgroup per (block, head, batch): the 3 x 64 token rows are read with
@@ -32,7 +32,7 @@ __global__ void __launch_bounds__(256) qkv_split_kernel(const Geo g, int heads,
                                                         __bf16* __restrict__ k,
                                                         __bf16* __restrict__ vt,
                                                         float* __restrict__ qbar,
-                                                        float* __restrict__ kbar) {
+                                                        __bf16* __restrict__ kbar) {
   using S = PoolShape<__bf16, D>;
   constexpr int kChunks = D / 8;                 // 16-byte chunks per token row
   constexpr int kStride = D + 8;                 // LDS row stride (elements)
@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(256) qkv_split_kernel(const Geo g, int heads,
     if (wave == 0)
       mask_detail::store_mean<__bf16, D>(mean, qbar + (head * g.nb + b) * D);
     else
-      mask_detail::store_mean_tiled<__bf16, D>(mean, kbar + head * kbar_rows(g.nb) * D, b);
+      mask_detail::store_mean_tiled<__bf16, D>(mean, kbar + head * kbar_head_elems(g.nb, D), b);
   }
 
   // V^T: row = channel, keys permuted inside each group of 16 by swapping
@@ -109,7 +109,7 @@ __global__ void __launch_bounds__(256) qkv_split_kernel(const Geo g, int heads,
 }  // namespace
 
 hipError_t launch_qkv_split(const Geo& g, int batch, int heads, const void* qkv, void* q, void* k,
-                            void* vt, float* qbar, float* kbar, hipStream_t s) {
+                            void* vt, float* qbar, __bf16* kbar, hipStream_t s) {
   const dim3 grid((unsigned)g.nb, (unsigned)heads, (unsigned)batch);
   if (g.d == 64) {
     hipLaunchKernelGGL(qkv_split_kernel<64>, grid, dim3(256), 0, s, g, heads,

@@ -64,11 +64,16 @@
  *   Q, K, V and O of one call share one layout, contiguous; Q, K, V share
  *   `dtype` and O has `out_dtype`.
  *   Pooled queries qbar: float32 [B, heads, nb, d] (row c = block c).
- *   Pooled keys kbar: float32 [B, heads, nb16, d], nb16 = 16 * ceil(nb / 16),
- *        in the mask kernel's matrix-core operand order: blocks in tiles of
- *        16 rows, and inside tile j the value of block 16 j + i, channel c at
- *        float offset 16 j d + ((c / 16) * 4 + (c / 4) % 4) * 64 + 4 i + c % 4,
- *        so that one 16-byte-per-lane load of a wavefront is 1 KB contiguous.
+ *   Pooled keys kbar: 3 * nb16 * d bf16 values per head, [B, heads] heads
+ *        in a row, nb16 = 16 * ceil(nb / 16).  Each float32 mean x is held
+ *        exactly as three bf16 parts h = bf16(x), m = bf16(x - h),
+ *        l = bf16(x - h - m) (round to nearest even; the two differences are
+ *        exact in float32 and l equals the last one, so h + m + l == x, and
+ *        (h + m) + l evaluated in float32 gives x back).  The parts sit in the
+ *        mask kernel's matrix-core operand order: part p of block 16 j + i,
+ *        channel c at bf16 offset
+ *        (((j * (d / 32) + c / 32) * 3 + p) * 64 + ((c / 8) % 4) * 16 + i) * 8 + c % 8,
+ *        so that each 16-byte-per-lane load of a wavefront is 1 KB contiguous.
  *        Rows past nb are ignored on input and left unwritten on output.
  *   Masks: uint32 [B, heads, nb, nw], nw = ceil(nb / 32); block c of row r is
  *   kept iff bit (c % 32) of word (c / 32) is set.  Bits >= nb are zero.
@@ -91,7 +96,7 @@
 extern "C" {
 #endif
 
-#define NABLA_ABI_VERSION 4
+#define NABLA_ABI_VERSION 5
 
 enum nabla_status {
   NABLA_OK = 0,
@@ -145,14 +150,16 @@ int nabla_unflatten(const nabla_geom* geom, const void* x_blocked, void* x, void
 
 /* Block average pooling of Q and K ([GZ] Methodology, downsampling;
  * [LS] sec. 2 and 4): qbar[b, h, c, :] = mean of the valid tokens of block c,
- * accumulated in float32, and the same for kbar in its tiled order (see the
- * layouts above).  q, k in geom's layout and dtype. */
+ * accumulated in float32, and the same for kbar in its split, tiled encoding
+ * (see the layouts above).  q, k in geom's layout and dtype. */
 int nabla_pool(const nabla_geom* geom, const void* q, const void* k,
-               float* qbar, float* kbar, void* stream);
+               float* qbar, void* kbar, void* stream);
 
 /* Adaptive block mask ([GZ] Methodology, reduced attention + CDF
  * thresholding + hybrid integration with STA).  For every row r of every
- * head: s_c = qbar_r . kbar_c * (1 / sqrt(d)) in float32, p = softmax(s);
+ * head: s_c = qbar_r . kbar_c * (1 / sqrt(d)) to float32 accuracy (six
+ * bf16 products of the three-part splits of qbar and kbar, float32
+ * accumulation), p = softmax(s);
  * the kept set is the smallest set of blocks taken in order of decreasing p
  * (ties: lower block index first) whose total probability reaches thr
  * (thr = 1 keeps every block).  If sta = {wt, wh, ww} is non-zero, every
@@ -167,7 +174,7 @@ int nabla_pool(const nabla_geom* geom, const void* q, const void* k,
  *   row_count      out, int32 [B, heads, nb]: kept blocks per row (union)
  *   adaptive_bits  optional out (may be NULL), uint32 [B, heads, nb, nw]:
  *                  the CDF-threshold mask before the STA union */
-int nabla_mask(const nabla_geom* geom, const float* qbar, const float* kbar,
+int nabla_mask(const nabla_geom* geom, const float* qbar, const void* kbar,
                float thr, const int32_t* sta, uint32_t* mask_bits,
                int32_t* row_count, uint32_t* adaptive_bits, void* stream);
 
@@ -189,7 +196,7 @@ int nabla_compact(const nabla_geom* geom, const uint32_t* mask_bits,
  * layout and dtype; thr and sta as for nabla_mask.  Arguments are checked
  * before anything is enqueued.  No workspace. */
 int nabla_mask_build(const nabla_geom* geom, const void* q, const void* k, float thr,
-                     const int32_t* sta, float* qbar, float* kbar, uint32_t* mask_bits,
+                     const int32_t* sta, float* qbar, void* kbar, uint32_t* mask_bits,
                      int32_t* row_count, uint32_t* adaptive_bits, int32_t* row_ptr,
                      int32_t* col_idx, void* stream);
 
@@ -232,11 +239,11 @@ int nabla_attn_fwd_vt(const nabla_geom* geom, const void* q, const void* k,
  *              order (pad slots included) its q, k and v rows of every head
  *   q, k       out, bf16 [B, heads, nb * 64, d]: copies, blocked layout
  *   vt         out, bf16 [B, heads, nb, d, 64]: as nabla_transpose_v of v
- *   qbar, kbar out, float32, layouts as for nabla_pool: bit-identical to nabla_pool
+ *   qbar, kbar out, layouts as for nabla_pool: bit-identical to nabla_pool
  *              of q and k (means over the valid tokens; pad slots ignored)
  * Bit-exact otherwise. */
 int nabla_qkv_split(const nabla_geom* geom, const void* qkv, void* q, void* k,
-                    void* vt, float* qbar, float* kbar, void* stream);
+                    void* vt, float* qbar, void* kbar, void* stream);
 
 /* Dense (full) attention, the baseline that the method's speed-ups are
  * measured against ([GZ] experimental results 1, speed-up over full

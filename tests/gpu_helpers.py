@@ -63,7 +63,7 @@ def run_pipeline(cfg: synth.Config, q, k, v, layout=nabla.LAYOUT_THW, thr=None, 
     dev = q.device
     B, h, nb, d = cfg.batch, cfg.heads, g.nb, cfg.head_dim
     qbar = torch.empty(nabla.qbar_shape(g), dtype=torch.float32, device=dev)
-    kbar = torch.empty(nabla.kbar_shape(g), dtype=torch.float32, device=dev)
+    kbar = torch.empty(nabla.kbar_shape(g), dtype=nabla.KBAR_DTYPE, device=dev)
     bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
     abits = torch.empty_like(bits)
     cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, f"{name} not exported"
         assert getattr(lib, name) is not None
-    assert lib.nabla_abi_version() == 4
+    assert lib.nabla_abi_version() == 5
 
 
 def G(**kw):
@@ -190,18 +190,51 @@ def test_probe_library_exports():
     assert lib.nabla_probe_mfma_bf16(0, 1, FAKE, None) == -1
 
 
+def _split3(x):
+    """Three-part bf16 encoding of float32 values, as include/nabla.h defines
+    it: h = bf16(x), m = bf16(x - h), l = bf16(x - h - m), round to nearest
+    even, differences in float32."""
+    import torch
+    h = x.to(torch.bfloat16)
+    r = x - h.to(torch.float32)
+    m = r.to(torch.bfloat16)
+    lo = (r - m.to(torch.float32)).to(torch.bfloat16)
+    return h, m, lo
+
+
+def test_kbar_split_is_exact():
+    """Every float32 mean survives its three-part encoding: h + m + l == x,
+    and (h + m) + l in float32 gives x back (normal magnitudes, both signs)."""
+    import torch
+    g = torch.Generator().manual_seed(7)
+    mant = torch.rand(200000, generator=g, dtype=torch.float64) + 1.0
+    expo = torch.randint(-60, 60, (200000,), generator=g).to(torch.float64)
+    sign = torch.where(torch.rand(200000, generator=g) < 0.5, -1.0, 1.0).to(torch.float64)
+    x = (sign * mant * torch.pow(2.0, expo)).to(torch.float32)
+    h, m, lo = _split3(x)
+    exact = h.to(torch.float64) + m.to(torch.float64) + lo.to(torch.float64)
+    assert torch.equal(exact, x.to(torch.float64))
+    back = (h.to(torch.float32) + m.to(torch.float32)) + lo.to(torch.float32)
+    assert torch.equal(back.view(torch.int32), x.view(torch.int32))
+
+
 def test_kbar_untile_follows_the_header_order():
-    """kbar_untile inverts the tiled order documented in include/nabla.h:
-    block 16 j + i, channel c at 16 j d + ((c / 16) * 4 + (c / 4) % 4) * 64 + 4 i + c % 4."""
+    """kbar_untile inverts the split, tiled encoding documented in
+    include/nabla.h: part p of block 16 j + i, channel c at bf16 offset
+    (((j * (d / 32) + c / 32) * 3 + p) * 64 + ((c / 8) % 4) * 16 + i) * 8 + c % 8."""
     import torch
     from block_sparse_attention_flatten_amd.api import kbar_untile
+    g = torch.Generator().manual_seed(3)
     for nb, d in ((37, 64), (48, 128)):
         nb16 = -(-nb // 16) * 16
-        flat = torch.full((nb16 * d,), -1.0, dtype=torch.float64)
+        want = torch.randn(nb, d, generator=g, dtype=torch.float32) * 3.0
+        h, m, lo = _split3(want)
+        flat = torch.full((3 * nb16 * d,), float("nan"), dtype=torch.bfloat16)
         for row in range(nb):
             for c in range(d):
-                off = (row // 16) * 16 * d + ((c // 16) * 4 + (c // 4) % 4) * 64 + 4 * (row % 16) + c % 4
-                flat[off] = row * 1000 + c
-        got = kbar_untile(flat.view(1, 1, nb16, d), nb)[0, 0]
-        want = torch.arange(nb, dtype=torch.float64)[:, None] * 1000 + torch.arange(d)[None, :]
-        assert torch.equal(got, want)
+                base = (((row // 16) * (d // 32) + c // 32) * 3 * 64 + ((c // 8) % 4) * 16
+                        + row % 16) * 8 + c % 8
+                for p, part in enumerate((h, m, lo)):
+                    flat[base + p * 64 * 8] = part[row, c]
+        got = kbar_untile(flat.view(1, 1, nb16, 3 * d), nb)[0, 0]
+        assert torch.equal(got.view(torch.int32), want.view(torch.int32))

@@ -101,7 +101,7 @@ def test_forward_and_backward_graph_replays_match_eager():
     def step():
         dev = q.device
         qbar = torch.empty(nabla.qbar_shape(g), dtype=torch.float32, device=dev)
-        kbar = torch.empty(nabla.kbar_shape(g), dtype=torch.float32, device=dev)
+        kbar = torch.empty(nabla.kbar_shape(g), dtype=nabla.KBAR_DTYPE, device=dev)
         bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
         cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)
         rp = torch.empty((B * h, nb + 1), dtype=torch.int32, device=dev)
@@ -176,7 +176,7 @@ def test_noalloc_and_layer_calls_graph_replays_match_eager():
         kb = torch.empty_like(qb)
         vt = torch.empty(nabla.vt_shape(gb), dtype=torch.bfloat16, device=dev)
         qbar = torch.empty(nabla.qbar_shape(g), dtype=torch.float32, device=dev)
-        kbar = torch.empty(nabla.kbar_shape(g), dtype=torch.float32, device=dev)
+        kbar = torch.empty(nabla.kbar_shape(g), dtype=nabla.KBAR_DTYPE, device=dev)
         bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
         cnt = torch.empty((B, h, nb), dtype=torch.int32, device=dev)
         rp = torch.empty((B * h, nb + 1), dtype=torch.int32, device=dev)

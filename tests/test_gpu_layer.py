@@ -54,7 +54,7 @@ def test_layer(name):
     k = torch.empty_like(q)
     vt = torch.empty(nabla.vt_shape(g), dtype=torch.bfloat16, device=dev)
     qbar = torch.empty(nabla.qbar_shape(g), dtype=torch.float32, device=dev)
-    kbar = torch.empty(nabla.kbar_shape(g), dtype=torch.float32, device=dev)
+    kbar = torch.empty(nabla.kbar_shape(g), dtype=nabla.KBAR_DTYPE, device=dev)
     nabla.nabla_qkv_split(g, qkv, q, k, vt, qbar, kbar)
     bits = torch.empty((B, h, nb, g.nw), dtype=torch.int32, device=dev)
     abits = torch.empty_like(bits)

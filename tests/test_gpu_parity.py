@@ -85,12 +85,12 @@ def test_pool(case, layout):
     else:
         qi, ki = q, k
     qbar = torch.empty(nabla.qbar_shape(g), device="cuda")
-    kbar = torch.full(nabla.kbar_shape(g), float("nan"), device="cuda")
+    kbar = torch.full(nabla.kbar_shape(g), float("nan"), dtype=nabla.KBAR_DTYPE, device="cuda")
     nabla.nabla_pool(g, qi, ki, qbar, kbar)
     torch.cuda.synchronize()
     og = ogeom(cfg)
     valid = O.valid_tokens(og)
-    # pooled keys come in the mask kernel's tiled order (every row written)
+    # pooled keys come split and tiled for the mask kernel (every row written)
     for x, xbar in ((q, qbar), (k, nabla.kbar_untile(kbar, g.nb))):
         ref = O.pool(O.flatten(f64(x), og), valid)
         got = f64(xbar)
