@@ -636,12 +636,15 @@ __device__ inline void cut_rows(const Geo& g, const MaskArgs& a, int64_t head, i
 }
 
 // ---------------------------------------------------------------------------
-// compaction of rows r0 .. r0 + n - 1 (n <= 64) of one head by one
+// compaction of rows r0 .. r0 + n - 1 (n <= kCompactRows) of one head by one
 // wavefront: the counts of all earlier rows of the head give the start, a
-// scan of the unit's own counts the row pointers; each row's bit words are
-// expanded with ballot + prefix popcount, so consecutive kept blocks go to
-// consecutive addresses.  Positions at or past the head's capacity nb * nb
-// are not written.
+// scan of the unit's own counts the row pointers.  Each row is expanded in
+// chunks of 64 blocks: lane l holds chunk l of the row (nb <= 4096, so one
+// 64-bit word per lane), a chunk read out with two readlanes IS the ballot of
+// its kept blocks, so lane j of chunk c writes block 64 c + j at the row's
+// position plus the kept blocks below it, and consecutive kept blocks go to
+// consecutive addresses.  Blocks >= nb and positions at or past the head's
+// capacity nb * nb are not written.
 // ---------------------------------------------------------------------------
 constexpr int kCompactRows = 16;   // rows per compaction unit
 
@@ -656,12 +659,19 @@ __device__ inline void compact_rows(const Geo& g, const CompactArgs& a, int64_t 
                                     int n) {
   const int nb = g.nb;
   const int nw = (nb + 31) >> 5;
+  const int nc = (nb + 63) >> 6;     // 64-block chunks per row
   const int lane = threadIdx.x & 63;
   const int32_t* cnt = a.count + head * nb;
   if (r0 + n > nb) n = nb - r0;
-  int s = 0;                         // kept blocks of all rows before r0
-  for (int i = lane; i < r0; i += 64) s += cnt[i];
-  const int base = wave_sum_i(s);
+  // kept blocks of all rows before r0: four independent loads in flight per lane
+  int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+  for (int i = lane; i < r0; i += 256) {
+    s0 += cnt[i];
+    if (i + 64 < r0) s1 += cnt[i + 64];
+    if (i + 128 < r0) s2 += cnt[i + 128];
+    if (i + 192 < r0) s3 += cnt[i + 192];
+  }
+  const int base = wave_sum_i((s0 + s1) + (s2 + s3));
   const int c = lane < n ? cnt[r0 + lane] : 0;
   int incl = c;                      // inclusive scan over the wavefront
 #pragma unroll
@@ -674,32 +684,33 @@ __device__ inline void compact_rows(const Geo& g, const CompactArgs& a, int64_t 
   if (lane < n) rp[r0 + lane] = start;
   if (lane == n - 1 && r0 + n == nb) rp[nb] = base + incl;   // the head's last row
   int32_t* out = a.col_idx + head * (int64_t)nb * nb;
-  const int cap = nb * nb;
-  // every row's words are loaded up front, so their latency is paid once
-  uint32_t w0s[kCompactRows], w1s[kCompactRows];
+  const uint32_t cap = (uint32_t)nb * (uint32_t)nb;
+  // every row's chunk words are loaded up front, so their latency is paid once
+  const int w0 = 2 * lane, w1 = w0 + 1;
+  uint32_t lo[kCompactRows], hi[kCompactRows];
 #pragma unroll
   for (int ri = 0; ri < kCompactRows; ++ri) {
     const uint32_t* wrow = a.bits + (head * nb + r0 + ri) * (int64_t)nw;
-    w0s[ri] = ri < n && lane < nw ? wrow[lane] : 0u;
-    w1s[ri] = ri < n && lane + 64 < nw ? wrow[lane + 64] : 0u;
+    lo[ri] = ri < n && w0 < nw ? wrow[w0] : 0u;
+    hi[ri] = ri < n && w1 < nw ? wrow[w1] : 0u;
   }
+  // blocks past nb in the last chunk are dropped
+  const int tail = nb - 64 * (nc - 1);
+  const uint64_t last_mask = tail >= 64 ? ~0ull : ((1ull << tail) - 1ull);
+  const uint64_t below = (1ull << lane) - 1ull;   // lanes below this one
 #pragma unroll
   for (int ri = 0; ri < kCompactRows; ++ri) {
-    if (ri >= n) break;
-    const uint32_t w0 = w0s[ri], w1 = w1s[ri];
-    int pos = __builtin_amdgcn_readlane(start, ri);
-    for (int c0 = 0; c0 < nb; c0 += 64) {
-      const int k = c0 >> 5;         // words k, k + 1 cover blocks c0 .. c0 + 63
-      const uint32_t wa = (uint32_t)__builtin_amdgcn_readlane((int)(k < 64 ? w0 : w1), k & 63);
-      const int k1 = k + 1;
-      const uint32_t wb =
-          k1 < nw ? (uint32_t)__builtin_amdgcn_readlane((int)(k1 < 64 ? w0 : w1), k1 & 63) : 0u;
-      const int col = c0 + lane;
-      const bool kept = col < nb && (((lane < 32 ? wa : wb) >> (lane & 31)) & 1u);
-      const uint64_t b = __ballot(kept);
-      const int at = pos + lanes_below(b);
-      if (kept && at >= 0 && at < cap) out[at] = col;
-      pos += __popcll(b);
+    if (ri < n) {                    // wavefront-uniform
+      uint32_t pos = (uint32_t)__builtin_amdgcn_readlane(start, ri);
+      for (int ch = 0; ch < nc; ++ch) {
+        uint64_t b = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lo[ri], ch) |
+                     ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi[ri], ch) << 32);
+        if (ch == nc - 1) b &= last_mask;
+        if (b == 0ull) continue;
+        const uint32_t at = pos + (uint32_t)__popcll(b & below);
+        if (((b >> lane) & 1ull) && at < cap) out[at] = 64 * ch + lane;
+        pos += (uint32_t)__popcll(b);
+      }
     }
   }
 }
