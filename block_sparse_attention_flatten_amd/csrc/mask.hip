@@ -45,18 +45,22 @@ hipError_t mask_t(const Geo& g, MaskArgs a, hipStream_t s) {
 }
 
 // Row-group shape of the standalone mask kernel by the number of blocks per
-// head: R rows per group (the R x nb float32 score tile must fit LDS, two
-// groups per CU up to nb = 1264), NW wavefronts, J = ceil(nb / 64) row
-// values per lane.
+// head: R rows per group (the R x nb float32 score tile must fit LDS), NW
+// wavefronts, J = ceil(nb / 64) row values per lane.  Up to nb = 1264 two
+// 16-row groups fit a CU; above that a 16-row tile leaves room for one group
+// per CU, whose score and cut phases then never overlap, and 8-row groups
+// (two or more per CU, at twice the pooled-key reads) are faster: 1.66 vs
+// 1.70 ms for the 2460-block mask construction, while at 1260 blocks 8-row
+// groups lose (0.65 vs 0.57 ms).
 template <int D, typename F>
 hipError_t dispatch_shape(int nb, const F& f) {
   if (nb <= 256) return f.template operator()<D, 16, 8, 4>();
   if (nb <= 512) return f.template operator()<D, 16, 8, 8>();
   if (nb <= 1024) return f.template operator()<D, 16, 8, 16>();
   if (nb <= 1280) return f.template operator()<D, 16, 8, 20>();
-  if (nb <= 1536) return f.template operator()<D, 16, 16, 24>();
-  if (nb <= 2048) return f.template operator()<D, 16, 16, 32>();
-  if (nb <= 2496) return f.template operator()<D, 16, 16, 39>();
+  if (nb <= 1536) return f.template operator()<D, 8, 8, 24>();
+  if (nb <= 2048) return f.template operator()<D, 8, 8, 32>();
+  if (nb <= 2496) return f.template operator()<D, 8, 8, 39>();
   if (nb <= 3072) return f.template operator()<D, 8, 8, 48>();
   return f.template operator()<D, 8, 8, 64>();
 }
