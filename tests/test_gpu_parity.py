@@ -98,6 +98,39 @@ def test_pool(case, layout):
         assert np.abs(got - ref).max() <= bound, (name, np.abs(got - ref).max(), bound)
 
 
+# One call per row-group shape of the mask kernel that the cases above do
+# not reach: blocks per head in (256, 512], (1280, 1536], (1536, 2048] and
+# (2496, 3072] (the 480p, 720p, Long and 3840-block shapes are covered by
+# test_gpu_fullsize.py).  One head, masks and lists only.
+MASK_SHAPES = {
+    "nb320_d64": dict(heads=1, T=4, H=64, W=80, head_dim=64, thr=0.7, sta=(3, 3, 3)),
+    "nb1440": dict(heads=1, T=6, H=96, W=160, thr=0.7, sta=(3, 3, 3)),
+    "nb1920": dict(heads=1, T=8, H=90, W=160, thr=0.8, sta=(1, 3, 3)),
+    "nb2880": dict(heads=1, T=12, H=96, W=153, thr=0.6, sta=(3, 3, 3)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MASK_SHAPES))
+def test_mask_shapes(name):
+    cfg = synth.config("small", **MASK_SHAPES[name])
+    log(f"mask shape {name}: {cfg}")
+    q, k, v = synth.make_qkv(cfg, device="cuda")
+    res = run_pipeline(cfg, q, k, v)
+    nb = res["g"].nb
+    union = unpack_bits(res["bits"], nb)[0, 0]
+    adapt = unpack_bits(res["abits"], nb)[0, 0]
+    cnt = res["cnt"].cpu().numpy()[0, 0]
+    rp = res["rp"].cpu().numpy()[0]
+    ci = res["ci"].cpu().numpy()[0]
+    ref = oracle_mask(cfg, f64(q[0, 0]), f64(k[0, 0]))
+    nbnd, ndf = check_mask_rows(union, adapt, ref, cfg.thr, name)
+    assert np.array_equal(cnt, union.sum(1))
+    assert rp[0] == 0 and np.array_equal(np.diff(rp), cnt)
+    for r in range(nb):
+        assert np.array_equal(ci[rp[r]:rp[r + 1]], np.flatnonzero(union[r])), (name, r)
+    log(f"mask shape {name}: nb {nb}, kept {union.mean():.3f}, band {nbnd}, differing {ndf}")
+
+
 def test_mask_and_forward(case):
     """pool -> mask -> compact -> attention through the C ABI vs the oracle."""
     name, cfg, q, k, v = case
