@@ -5,8 +5,9 @@
 // HBM-bound streaming read, one wavefront per block (pool_block in
 // mask_items.hpp; nabla_qkv_split repeats its summation order, so both give
 // the same bits).  The pooled keys are written as the mask kernel reads
-// them: each mean as three exact bf16 parts, in its tiled order.  Both the natural and the blocked layout are addressed in 8-token
-// patch rows, so the reorder costs no extra pass.
+// them: each mean as three exact bf16 parts, in its tiled order.  Both the
+// natural and the blocked layout are addressed in 8-token patch rows, so the
+// reorder costs no extra pass.
 #include "mask_items.hpp"
 
 namespace nabla {
